@@ -1,0 +1,115 @@
+"""Seeded synthetic inputs for single-precision GEMM.
+
+This module holds the workload table and the random-input recipes, and nothing
+of the GEMM arithmetic.  Both the HIP path's tests/benchmark and the CPU
+oracle's tests take their arrays from here, so the two sides see the same
+bytes.
+
+Recipe (the pages give no seeds or generator; every page times square
+4096 x 4096 x 4096 products only, e.g. "Warp Tiling: A Third Level of Tiling",
+section "Mechanics"):
+  * generator ``numpy.random.default_rng(seed)`` (PCG64);
+  * draw order A (M x K), then B (K x N), then C (M x N) when C is random;
+  * U[-1,1]: ``rng.uniform(-1, 1, shape)`` rounded to float32;
+  * N(0,1):  ``rng.standard_normal(shape, dtype=float32)``;
+  * tight row-major layout (lda = K, ldb = N, ldc = N).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    M: int
+    N: int
+    K: int
+    dist: str          # "uniform" (U[-1,1]) or "normal" (N(0,1)) for A and B
+    c_init: str        # "zero" or "uniform"
+    alpha: float
+    beta: float
+    seed: int
+
+    @property
+    def flops(self) -> int:
+        """2*M*N*K, the pages' operation count (epilogue not counted)."""
+        return 2 * self.M * self.N * self.K
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("sq256", 256, 256, 256, "uniform", "zero", 1.0, 0.0, 1),
+        Workload("sq1024", 1024, 1024, 1024, "uniform", "uniform", 0.5, 3.0, 2),
+        Workload("sq2048", 2048, 2048, 2048, "uniform", "uniform", 0.5, 3.0, 3),
+        Workload("sq4096", 4096, 4096, 4096, "uniform", "uniform", 0.5, 3.0, 4),
+        Workload("tall8192x2048x4096", 8192, 2048, 4096, "normal", "zero", 1.0, 0.0, 5),
+        Workload("ragged1000x1500x777", 1000, 1500, 777, "uniform", "uniform", 1.0, 1.0, 6),
+        Workload("ragged4097x4095x4093", 4097, 4095, 4093, "uniform", "uniform", 1.0, 1.0, 7),
+        Workload("sq8192", 8192, 8192, 8192, "uniform", "zero", 1.0, 0.0, 8),
+    ]
+}
+
+# The headline workload the throughput metric is quoted on.
+HEADLINE = "sq4096"
+
+
+def _draw(rng: np.random.Generator, dist: str, shape) -> np.ndarray:
+    if dist == "uniform":
+        return rng.uniform(-1.0, 1.0, size=shape).astype(np.float32)
+    if dist == "normal":
+        return rng.standard_normal(size=shape, dtype=np.float32)
+    raise ValueError(dist)
+
+
+def make(w: Workload | str):
+    """Return (A, B, C) as C-contiguous float32 arrays for a workload."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    return make_random(w.M, w.N, w.K, w.seed, w.dist, w.c_init)
+
+
+def make_random(M, N, K, seed, dist="uniform", c_init="uniform"):
+    rng = np.random.default_rng(seed)
+    A = _draw(rng, dist, (M, K))
+    B = _draw(rng, dist, (K, N))
+    if c_init == "zero":
+        C = np.zeros((M, N), dtype=np.float32)
+    elif c_init == "uniform":
+        C = _draw(rng, "uniform", (M, N))
+    else:
+        raise ValueError(c_init)
+    return A, B, C
+
+
+def make_small_int(M, N, K, seed, lo=-4, hi=4):
+    """Integer-valued float32 inputs drawn uniformly from {lo..hi}.
+
+    With |values| <= 4 every partial sum of K products stays an integer below
+    2**24 for K < 2**20, so any summation order gives the same fp32 result.
+    """
+    rng = np.random.default_rng(seed)
+    A = rng.integers(lo, hi + 1, size=(M, K)).astype(np.float32)
+    B = rng.integers(lo, hi + 1, size=(K, N)).astype(np.float32)
+    C = rng.integers(lo, hi + 1, size=(M, N)).astype(np.float32)
+    return A, B, C
+
+
+def sample_indices(M, N, count, seed, tile=(256, 256)):
+    """Output positions for sampled checks at sizes the CPU oracle cannot
+    finish in full: random entries plus every tile corner and the last row and
+    column (the ragged edges)."""
+    rng = np.random.default_rng(seed)
+    rows = list(rng.integers(0, M, size=count))
+    cols = list(rng.integers(0, N, size=count))
+    tm, tn = tile
+    for r in sorted({0, M - 1} | set(range(tm - 1, M, tm)) | set(range(tm, M, tm))):
+        for c in (0, N - 1, min(tn, N - 1), min(tn - 1, N - 1)):
+            rows.append(r); cols.append(c)
+    for c in sorted({0, N - 1} | set(range(tn - 1, N, tn)) | set(range(tn, N, tn))):
+        rows.append(M - 1); cols.append(c)
+        rows.append(0); cols.append(c)
+    return np.asarray(rows, dtype=np.int64), np.asarray(cols, dtype=np.int64)
