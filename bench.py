@@ -1,0 +1,200 @@
+"""Benchmark: fp32 SGEMM throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--cfg ID]
+
+A step is one C = alpha*A*B + beta*C call of the library (the whole hot path)
+on the workload's seeded inputs, already resident in device memory.  Each
+step writes its own copy of the pristine C, so every timed launch does the
+full read-modify-write on fresh data and the last output can be checked
+against the CPU oracle.  Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fp32 SGEMM GFLOP/s at 4096^3 and % of MI355X fp32 peak (1 GPU)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="sq4096")
+    ap.add_argument("--cfg", type=int, default=-1, help="force a configuration id")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-context", action="store_true", help="skip timing torch.mm")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 28  # 2^28 floats = 1 GiB
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_way": 4 * n, "launches": 3}), flush=True)
+
+
+def cpu_baseline(w, A, B, C, target_s):
+    """The oracle, as it stands, on the first R rows of the same workload."""
+    from oracle import oracle
+    oracle.build(force=False)
+    threads = oracle.max_threads()
+    rows = 8
+    t0 = time.perf_counter()
+    oracle.sgemm(A[:rows], B, C[:rows], w.alpha, w.beta)
+    probe = time.perf_counter() - t0
+    rows = int(max(8, min(w.M, rows * max(1.0, (target_s - probe) / max(probe, 1e-3)))))
+    t0 = time.perf_counter()
+    oracle.sgemm(A[:rows], B, C[:rows], w.alpha, w.beta)
+    dt = time.perf_counter() - t0
+    gflops = 2.0 * rows * w.N * w.K / dt / 1e9
+    return {"value": round(gflops, 3), "unit": "GFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {rows} of {w.M} rows of the same {w.M}x{w.N}x{w.K} product "
+                      f"(fp64 accumulation, OpenMP over rows), {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} "
+              f"(WORLD_SIZE={world}) is not supported", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import fp32_gemm_amd as fg
+    from fp32_gemm_amd import inputs, model
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if fg.device_check() != 0:
+        raise SystemExit("bench.py: current device is not gfx950")
+    w = inputs.WORKLOADS[args.workload]
+    A, B, C = inputs.make(w)
+    Ad = torch.from_numpy(A).to(dev)
+    Bd = torch.from_numpy(B).to(dev)
+    C0 = torch.from_numpy(C).to(dev)
+    total = args.warmup + args.steps
+    pool = min(total, 64)
+    Cs = [C0.clone() for _ in range(pool)]
+    stream = torch.cuda.current_stream(dev)
+    plan = fg.binding.plan(w.M, w.N, w.K, Ad.data_ptr(), w.K, Bd.data_ptr(), w.N,
+                           Cs[0].data_ptr(), w.N, args.cfg)
+    info = fg.config_info(plan["cfg_id"])
+
+    def step(i):
+        fg.sgemm_ex(Ad, Bd, Cs[i % pool], w.alpha, w.beta, stream=stream, cfg_id=args.cfg)
+
+    for i in range(args.warmup):
+        step(i)
+    # Refill the buffers the timed steps will use with the pristine C.
+    for i in range(args.steps):
+        Cs[(args.warmup + i) % pool].copy_(C0)
+    torch.cuda.synchronize()
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])  # ms
+    avg_ms = float(ev[0].elapsed_time(ev[-1])) / args.steps
+
+    # Parity of the last timed output against the oracle on sampled entries.
+    from oracle import oracle
+    last = Cs[(total - 1) % pool].cpu().numpy()
+    rows, cols = inputs.sample_indices(w.M, w.N, 2000, seed=w.seed + 100)
+    _, e64 = oracle.entries(rows, cols, A, B, C, w.alpha, w.beta)
+    parity = oracle.rel_error(last[rows, cols], e64, w.K, np.abs(A).max(), np.abs(B).max())
+
+    flops = model.flops(w.M, w.N, w.K)
+    value = flops * args.steps / wall / 1e9
+    achieved = flops / (avg_ms * 1e-3) / 1e12
+    peak = model.PEAK_FP32_TFLOPS
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tpath):
+        with open(tpath) as f:
+            tr = json.load(f)
+        key = f"{args.workload}:{'/'.join(map(str, info['tuple']))}"
+        if key in tr:
+            traffic = tr[key]["bytes_per_launch"]
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"sgemm {w.M}x{w.N}x{w.K} alpha={w.alpha} beta={w.beta} "
+                        f"A,B ~ {'U[-1,1]' if w.dist == 'uniform' else 'N(0,1)'} seed {w.seed}",
+            "M": w.M, "N": w.N, "K": w.K, "alpha": w.alpha, "beta": w.beta,
+            "cfg_id": info["id"], "path": info["path_name"], "tile": list(info["tuple"]),
+            "vector_variant": plan["vector_variant"], "grid": plan["grid"],
+        },
+        "pct_of_peak": round(100.0 * value / 1e3 / peak, 2),
+        "roofline": {
+            "bound": "mfma" if info["path"] != 0 else "alu",
+            "achieved": round(achieved, 2),
+            "peak": round(peak if info["path"] != 0 else model.PEAK_FP32_VALU_UNPACKED_TFLOPS, 1),
+            "unit": "TFLOP/s",
+            "frac": round(achieved / (peak if info["path"] != 0 else model.PEAK_FP32_VALU_UNPACKED_TFLOPS), 4),
+            "traffic": traffic,
+        },
+        "timing_ms": {"event_avg": round(avg_ms, 4), "median": round(float(np.median(per)), 4),
+                      "min": round(float(per.min()), 4), "max": round(float(per.max()), 4),
+                      "spread": round(float((per.max() - per.min()) / np.median(per)), 4)},
+        "parity_err": parity,
+    }
+    if not args.no_context:
+        Cm = torch.empty_like(C0)
+        for _ in range(3):
+            torch.mm(Ad, Bd, out=Cm)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            torch.mm(Ad, Bd, out=Cm)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out["context"] = {"torch_mm_tflops": round(flops / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e12, 2),
+                          "note": "vendor BLAS timing, context only; never used for dispatch or parity"}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, A, B, C, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -8,15 +8,16 @@ supplies device memory and streams.
 The binding is loaded on first use of an API name, so ``fp32_gemm_amd.inputs``
 can be imported on a machine where the library has not been built.
 """
-_API = ("sgemm", "sgemm_ex", "sgemm_raw", "num_configs", "config_info", "configs",
+_API = ("sgemm", "sgemm_ex", "sgemm_raw", "plan", "num_configs", "config_info", "configs",
         "status_string", "device_check", "SgemmError", "library_path", "check_tuple",
         "simulate_tuple", "exported_symbols")
 
 
 def __getattr__(name):
-    if name in _API:
-        from . import binding
-        return getattr(binding, name)
+    if name == "binding" or name in _API:
+        import importlib
+        binding = importlib.import_module(__name__ + ".binding")
+        return binding if name == "binding" else getattr(binding, name)
     raise AttributeError(name)
 
 

@@ -1,0 +1,228 @@
+"""ctypes binding of libfp32_gemm_amd.so (argument marshalling only).
+
+Every step of the computation runs in the library's HIP kernels; this module
+only checks tensor metadata, turns tensors into (pointer, leading dimension)
+pairs and maps status codes to exceptions.  There is no fallback: if the
+library is missing, importing this module raises.
+
+torch is imported before the library is opened so that the library binds to
+the HIP runtime torch has already loaded (both carry the same soname), which
+makes torch's device pointers and stream handles valid for the library.
+"""
+from __future__ import annotations
+
+import ctypes
+import json
+import os
+import re
+
+import torch  # noqa: F401  -- must load torch's HIP runtime first (see above)
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libfp32_gemm_amd.so")
+_RESOURCES = os.path.join(_PKG, "_build", "resources.json")
+
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(
+        f"{_LIB_PATH} is not built; run `python -m fp32_gemm_amd.build` (hipcc, gfx950)")
+
+_lib = ctypes.CDLL(_LIB_PATH)
+
+_i64, _i32, _f32, _vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [(n, _i32) for n in (
+        "id", "path", "BM", "BN", "BK", "WM", "WN", "WNITER", "TM", "TN", "NT", "swz",
+        "WMITER", "WSUBM", "WSUBN", "acc_per_lane", "lds_bytes", "vgpr_estimate")]
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [("cfg_id", _i32), ("vector_variant", _i32), ("grid", _i64), ("block", _i32)]
+
+
+class _Attr(ctypes.Structure):
+    _fields_ = [("num_regs", _i32), ("scratch_bytes", _i32), ("lds_bytes", _i32),
+                ("max_threads", _i32)]
+
+
+class _SimReport(ctypes.Structure):
+    _fields_ = [("failed_check", _i32), ("store_a_ways", _i32), ("store_b_ways", _i32),
+                ("read_a_ways", _i32), ("read_b_ways", _i32)]
+
+
+_SIGS = {
+    "sgemm": ([_i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64], ctypes.c_int),
+    "sgemm_ex": ([_i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64, _vp, _i32],
+                 ctypes.c_int),
+    "sgemm_num_configs": ([], ctypes.c_int),
+    "sgemm_config_info": ([_i32, ctypes.POINTER(_Config)], ctypes.c_int),
+    "sgemm_plan": ([_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i32,
+                    ctypes.POINTER(_Plan)], ctypes.c_int),
+    "sgemm_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "sgemm_last_hip_error": ([], ctypes.c_int),
+    "sgemm_device_check": ([], ctypes.c_int),
+    "sgemm_kernel_attributes": ([_i32, _i32, ctypes.POINTER(_Attr)], ctypes.c_int),
+    "sgemm_check_tuple": ([ctypes.POINTER(_i32), _i32], ctypes.c_int),
+    "sgemm_simulate_tuple": ([ctypes.POINTER(_i32), _i32, ctypes.POINTER(_SimReport)],
+                             ctypes.c_int),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+PATHS = {0: "valu", 1: "mfma32", 2: "mfma16"}
+TUPLE_FIELDS = ("BM", "BN", "BK", "WM", "WN", "WNITER", "TM", "TN", "NT", "path", "swz")
+
+
+class SgemmError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        msg = _lib.sgemm_status_string(status).decode()
+        if status == 4:
+            msg += f" (hipError_t {_lib.sgemm_last_hip_error()})"
+        super().__init__(f"sgemm status {status}: {msg}")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def exported_symbols():
+    """Names declared in include/fp32_gemm.h that the library must export."""
+    return sorted(_SIGS)
+
+
+def status_string(status: int) -> str:
+    return _lib.sgemm_status_string(status).decode()
+
+
+def device_check() -> int:
+    return _lib.sgemm_device_check()
+
+
+def num_configs() -> int:
+    return _lib.sgemm_num_configs()
+
+
+def config_info(cfg_id: int) -> dict:
+    c = _Config()
+    rc = _lib.sgemm_config_info(cfg_id, ctypes.byref(c))
+    if rc != 0:
+        raise SgemmError(rc)
+    d = {f: getattr(c, f) for f, _ in _Config._fields_}
+    d["tuple"] = tuple(d[f] for f in TUPLE_FIELDS)
+    d["path_name"] = PATHS[d["path"]]
+    return d
+
+
+def _kernel_resources():
+    """Compiler resource report per tuple and variant, if the build left one."""
+    if not os.path.exists(_RESOURCES):
+        return {}
+    with open(_RESOURCES) as f:
+        raw = json.load(f)
+    out = {}
+    pat = re.compile(r"TileCfgILi" + r"ELi".join([r"(\d+)"] * 11) + r"EEELb(\d)")
+    for name, v in raw.items():
+        m = pat.search(name)
+        if m:
+            g = tuple(int(x) for x in m.groups())
+            out[(g[:11], g[11])] = v
+    return out
+
+
+def configs():
+    """All compiled configurations, with the compiler's resource report."""
+    res = _kernel_resources()
+    out = []
+    for i in range(num_configs()):
+        d = config_info(i)
+        d["resources_vec"] = res.get((d["tuple"], 1))
+        d["resources_scalar"] = res.get((d["tuple"], 0))
+        out.append(d)
+    return out
+
+
+def kernel_attributes(cfg_id: int, vector_variant: bool = True) -> dict:
+    a = _Attr()
+    rc = _lib.sgemm_kernel_attributes(cfg_id, int(vector_variant), ctypes.byref(a))
+    if rc != 0:
+        raise SgemmError(rc)
+    return {f: getattr(a, f) for f, _ in _Attr._fields_}
+
+
+def check_tuple(tup, target: str = "gfx950") -> int:
+    arr = (_i32 * 11)(*tup)
+    return _lib.sgemm_check_tuple(arr, {"gfx950": 0, "page": 1}[target])
+
+
+def simulate_tuple(tup, banks: int = 32) -> dict:
+    arr = (_i32 * 11)(*tup)
+    r = _SimReport()
+    rc = _lib.sgemm_simulate_tuple(arr, banks, ctypes.byref(r))
+    d = {f: getattr(r, f) for f, _ in _SimReport._fields_}
+    d["status"] = rc
+    return d
+
+
+def sgemm_raw(M, N, K, alpha, A_ptr, lda, B_ptr, ldb, beta, C_ptr, ldc, stream=None, cfg_id=-1):
+    """Direct call of sgemm_ex on raw device pointers; returns the status."""
+    return _lib.sgemm_ex(M, N, K, alpha, A_ptr, lda, B_ptr, ldb, beta, C_ptr, ldc,
+                         stream, cfg_id)
+
+
+def plan(M, N, K, A_ptr, lda, B_ptr, ldb, C_ptr, ldc, cfg_id=-1) -> dict:
+    p = _Plan()
+    rc = _lib.sgemm_plan(M, N, K, A_ptr, lda, B_ptr, ldb, C_ptr, ldc, cfg_id, ctypes.byref(p))
+    if rc != 0:
+        raise SgemmError(rc)
+    return {f: getattr(p, f) for f, _ in _Plan._fields_}
+
+
+def _operand(t, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride (row-major)")
+    ld = t.stride(0) if t.shape[0] > 1 else max(t.shape[1], 1)
+    return t.data_ptr(), max(ld, t.shape[1], 1)
+
+
+def sgemm_ex(A, B, C, alpha=1.0, beta=0.0, stream=None, cfg_id=-1):
+    """C <- alpha * A @ B + beta * C in place, for float32 GPU tensors.
+
+    A is M x K, B is K x N, C is M x N, each row-major with unit column stride
+    (a row slice of a wider buffer is fine: its row stride is the leading
+    dimension).  The call is asynchronous on `stream` (default: torch's
+    current stream on C's device).  Returns C.
+    """
+    a, lda = _operand(A, "A")
+    b, ldb = _operand(B, "B")
+    c, ldc = _operand(C, "C")
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K or tuple(C.shape) != (M, N):
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, C {tuple(C.shape)}")
+    if not (A.device == B.device == C.device):
+        raise ValueError("A, B and C must be on the same device")
+    if stream is None:
+        stream = torch.cuda.current_stream(C.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    with torch.cuda.device(C.device):
+        rc = _lib.sgemm_ex(M, N, K, alpha, a, lda, b, ldb, beta, c, ldc, handle, cfg_id)
+    if rc != 0:
+        raise SgemmError(rc)
+    return C
+
+
+def sgemm(A, B, C, alpha=1.0, beta=0.0):
+    """Tuned-dispatch SGEMM on torch's current stream (see :func:`sgemm_ex`)."""
+    return sgemm_ex(A, B, C, alpha, beta)

@@ -1,0 +1,181 @@
+"""Build libfp32_gemm_amd.so (HIP for gfx950) in-tree.
+
+The candidate tile tuples below are written into generated instance
+translation units; each candidate passes through the C++ legality checker at
+compile time and only legal ones instantiate kernels.  The units compile in
+parallel with hipcc and link into ``fp32_gemm_amd/libfp32_gemm_amd.so``.  The
+compiler's per-kernel resource report (VGPRs, AGPRs, scratch, occupancy) is
+saved to ``fp32_gemm_amd/_build/resources.json``.
+
+Usage: ``python -m fp32_gemm_amd.build`` (or ``__graft_entry__.build()``).
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import json
+import os
+import re
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libfp32_gemm_amd.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+# Packed-FP32 VALU instructions are kept out of every kernel (the
+# target-feature switch below); hipcc's host pass warns that it does not know
+# the feature, which is harmless.
+HIP_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+
+VALU, MFMA32, MFMA16 = 0, 1, 2
+
+
+def candidates():
+    """Candidate tuples (BM, BN, BK, WM, WN, WNITER, TM, TN, NT, path, swz)."""
+    out = []
+    # MFMA 32x32x2: every block/warp tile split into 1, 2, 4 or 8 waves.
+    for BM, BN in [(256, 256), (256, 128), (128, 256), (128, 128), (128, 64), (64, 128), (64, 64)]:
+        for BK in (8, 16, 32):
+            for WM in (32, 64, 128):
+                for WN in (32, 64, 128):
+                    if WM > BM or WN > BN:
+                        continue
+                    waves = (BM // WM) * (BN // WN)
+                    if waves not in (1, 2, 4, 8):
+                        continue
+                    out.append((BM, BN, BK, WM, WN, WN // 32, 16, 1, 64 * waves, MFMA32, 32))
+    # MFMA 16x16x4: a few block shapes.
+    for BM, BN, WM, WN in [(128, 128, 64, 64), (256, 128, 128, 64), (256, 256, 128, 128),
+                           (64, 64, 32, 32), (128, 64, 64, 32)]:
+        for BK in (16, 32):
+            waves = (BM // WM) * (BN // WN)
+            out.append((BM, BN, BK, WM, WN, WN // 16, 4, 1, 64 * waves, MFMA16, 32))
+    # VALU outer products: wave64 analogues of the page's shapes.
+    for t in [
+        (128, 128, 8, 64, 64, 1, 8, 8, 256),    # the page's square 128x128 tile, 8x8 lanes
+        (128, 128, 16, 64, 64, 1, 8, 8, 256),
+        (128, 64, 16, 64, 64, 2, 4, 4, 128),    # the page's winning shape, WN widened for 64 lanes
+        (128, 64, 8, 64, 64, 2, 4, 4, 128),
+        (128, 128, 16, 64, 64, 2, 4, 4, 256),
+        (64, 64, 16, 64, 64, 2, 4, 4, 64),
+        (128, 128, 16, 128, 64, 2, 8, 4, 128),
+        (256, 128, 16, 128, 64, 2, 8, 4, 256),
+        (128, 128, 32, 64, 64, 2, 4, 4, 256),
+    ]:
+        out.append(t + (VALU, 32))
+    # Bank-model variants of the headline shapes: unswizzled, and 64 banks.
+    for base in [(256, 256, 16, 128, 128, 4, 16, 1, 256, MFMA32),
+                 (128, 128, 16, 64, 64, 2, 16, 1, 256, MFMA32),
+                 (128, 128, 16, 64, 64, 4, 4, 1, 256, MFMA16),
+                 (128, 64, 16, 64, 64, 2, 4, 4, 128, VALU)]:
+        out.append(base + (0,))
+        out.append(base + (64,))
+    seen, uniq = set(), []
+    for t in out:
+        if t not in seen:
+            seen.add(t)
+            uniq.append(t)
+    return uniq
+
+
+def _write_if_changed(path, text):
+    if os.path.exists(path):
+        with open(path) as f:
+            if f.read() == text:
+                return
+    with open(path, "w") as f:
+        f.write(text)
+
+
+def generate(n_units=16):
+    os.makedirs(BUILD, exist_ok=True)
+    cands = candidates()
+    units = [cands[i::n_units] for i in range(n_units)]
+    units = [u for u in units if u]
+    srcs = []
+    for ui, unit in enumerate(units):
+        lines = ['#include "registry.hpp"', "namespace fp32gemm {",
+                 f"extern ConfigEntry kEntries{ui}[] = {{"]
+        for t in unit:
+            lines.append("  candidate<%s>()," % ", ".join(str(x) for x in t))
+        lines += ["};", f"extern const int kCount{ui} = {len(unit)};", "}  // namespace fp32gemm", ""]
+        path = os.path.join(BUILD, f"instances_{ui:02d}.hip")
+        _write_if_changed(path, "\n".join(lines))
+        srcs.append(path)
+    idx = ["namespace fp32gemm {"]
+    for ui in range(len(units)):
+        idx.append(f"extern ConfigEntry kEntries{ui}[]; extern const int kCount{ui};")
+    idx.append("static const EntryTable kTables[] = {")
+    for ui in range(len(units)):
+        idx.append(f"  {{kEntries{ui}, kCount{ui}}},")
+    idx += ["};", "}  // namespace fp32gemm", ""]
+    # kCount is a run-time value across units; the table is read after static init.
+    _write_if_changed(os.path.join(BUILD, "instances_index.inc"), "\n".join(idx))
+    return srcs
+
+
+_REMARK = re.compile(r"remark: (?:\s*)(Function Name|TotalSGPRs|VGPRs|AGPRs|ScratchSize \[bytes/lane\]|"
+                     r"Occupancy \[waves/SIMD\]|LDS Size \[bytes/block\]): (\S+)")
+
+
+def _compile(src, obj, remarks):
+    cmd = [HIPCC, *HIP_FLAGS, "-I", CSRC, "-I", BUILD, "-c", src, "-o", obj]
+    if remarks:
+        cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
+    p = subprocess.run(cmd, capture_output=True, text=True)
+    if p.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{p.stderr[-6000:]}")
+    res, cur = {}, None
+    for m in _REMARK.finditer(p.stderr):
+        key, val = m.group(1), m.group(2)
+        if key == "Function Name":
+            cur = val
+            res[cur] = {}
+        elif cur is not None:
+            res[cur][key.split(" ")[0]] = int(val)
+    return res
+
+
+def build(verbose=True, jobs=None):
+    """Compile every HIP source for gfx950 and link the shared library."""
+    t_srcs = generate()
+    jobs = jobs or min(16, os.cpu_count() or 4)
+    api = os.path.join(CSRC, "sgemm_api.hip")
+    work = [(api, os.path.join(BUILD, "sgemm_api.o"), False)]
+    work += [(s, s[:-4] + ".o", True) for s in t_srcs]
+    resources = {}
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        futs = {ex.submit(_compile, s, o, r): s for s, o, r in work}
+        for f in cf.as_completed(futs):
+            resources.update(f.result())
+            if verbose:
+                print(f"[build] compiled {os.path.basename(futs[f])}", flush=True)
+    tmp = LIB + ".tmp%d" % os.getpid()
+    link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + [o for _, o, _ in work]
+    p = subprocess.run(link, capture_output=True, text=True)
+    if p.returncode != 0:
+        raise RuntimeError("link failed:\n" + p.stderr[-4000:])
+    os.replace(tmp, LIB)
+    with open(os.path.join(BUILD, "resources.json"), "w") as f:
+        json.dump(resources, f, indent=1, sort_keys=True)
+    spills = {k: v for k, v in resources.items() if v.get("ScratchSize", 0) > 0}
+    if verbose:
+        print(f"[build] {LIB}: {len(resources)} kernels, {len(spills)} with scratch", flush=True)
+    return LIB
+
+
+def clean():
+    shutil.rmtree(BUILD, ignore_errors=True)
+    if os.path.exists(LIB):
+        os.remove(LIB)
+
+
+if __name__ == "__main__":
+    build(verbose="-q" not in sys.argv)

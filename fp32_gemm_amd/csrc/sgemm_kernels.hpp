@@ -1,0 +1,356 @@
+// sgemm_kernels.hpp -- the gfx950 SGEMM kernel template.
+//
+// One workgroup computes one BM x BN tile of C = alpha*A*B + beta*C (the block
+// tile of "Warp Tiling: A Third Level of Tiling", section "The Kernel"); each
+// 64-lane wave owns a WM x WN warp tile split into WMITER x WNITER sub-tiles.
+// The K loop walks BK-wide slices:
+//
+//   prologue: stage slice 0 into LDS buffer 0, barrier
+//   for each slice kt:
+//       issue the global loads of slice kt+1 into registers
+//       inner product over buffer kt&1 (VALU outer products or MFMA blocks)
+//       write the registers of slice kt+1 into buffer (kt+1)&1
+//       barrier
+//   epilogue: C = alpha*acc + beta*C for in-range elements only
+//
+// With two LDS buffers one barrier per slice is enough: a buffer is only
+// rewritten one iteration after every wave has passed the barrier that ended
+// its last use (the page "Shared Memory Tiling" explains why a single buffer
+// needs a barrier on both sides of the inner product).
+//
+// Operands are read through buffer resources rebuilt per slice, so every load
+// is range-checked by the hardware; elements outside the logical M x K and
+// K x N windows are masked by giving them an offset past the resource's end,
+// which returns zero without touching memory.  The VEC variant moves float4s
+// and needs K % 4 == N % 4 == 0, lda % 4 == ldb % 4 == ldc % 4 == 0 and
+// 16-byte aligned pointers (checked by the host); the scalar variant moves
+// single floats with the same staging map and LDS layout and accepts any
+// shape and leading dimension.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tile_maps.hpp"
+
+namespace fp32gemm {
+
+struct KernelArgs {
+  const float* A;
+  const float* B;
+  float* C;
+  long long lda, ldb, ldc;
+  int M, N, K;
+  int tiles_n;  // ceil(N / BN): the 1-D grid is tiles_m * tiles_n workgroups
+  float alpha, beta;
+};
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Buffer resources never describe more than kMaxRecords bytes; a masked
+// element is loaded from kMaskedOffset, which is therefore always out of
+// range and reads as zero.
+constexpr long long kMaxRecords = 0x7FFFFFF0LL;
+constexpr int kMaskedOffset = 0x7FFFFFF0;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const float* base, long long bytes) {
+  const long long b = bytes < 0 ? 0 : (bytes > kMaxRecords ? kMaxRecords : bytes);
+  // Word 3 = 0x00020000: 32-bit data format, raw (unswizzled, stride 0) buffer.
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), static_cast<short>(0),
+                                           static_cast<int>(b), 0x00020000);
+}
+
+__device__ __forceinline__ f32x4 buffer_load4(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ float buffer_load1(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+template <class Cfg>
+struct Staged {
+  f32x4 a[Cfg::PASSES_A];
+  f32x4 b[Cfg::PASSES_B];
+};
+
+// Global -> registers for the slice starting at k0.
+template <class Cfg, bool VEC>
+__device__ __forceinline__ void stage_load(const KernelArgs& p, int row0, int col0, int k0, int t,
+                                           Staged<Cfg>& s) {
+  constexpr Geom g = make_geom(Cfg::tile);
+  const int lda = static_cast<int>(p.lda), ldb = static_cast<int>(p.ldb);
+
+  const int rows = min(g.BM, p.M - row0);
+  const float* abase = p.A + static_cast<long long>(row0) * p.lda + k0;
+  const auto ra = make_rsrc(abase, (static_cast<long long>(rows - 1) * p.lda + (p.K - k0)) * 4);
+#pragma unroll
+  for (int ps = 0; ps < g.PASSES_A; ++ps) {
+    const int m = stage_a_row(g, t, ps), c = 4 * stage_a_kq(g, t);
+    if constexpr (VEC) {
+      const bool ok = (m < rows) && (k0 + c < p.K);
+      s.a[ps] = buffer_load4(ra, ok ? (m * lda + c) * 4 : kMaskedOffset);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool ok = (m < rows) && (k0 + c + e < p.K);
+        s.a[ps][e] = buffer_load1(ra, ok ? (m * lda + c + e) * 4 : kMaskedOffset);
+      }
+    }
+  }
+
+  const int krows = min(g.BK, p.K - k0);
+  const float* bbase = p.B + static_cast<long long>(k0) * p.ldb + col0;
+  const auto rb = make_rsrc(bbase, (static_cast<long long>(krows - 1) * p.ldb + (p.N - col0)) * 4);
+#pragma unroll
+  for (int ps = 0; ps < g.PASSES_B; ++ps) {
+    const int k = stage_b_row(g, t, ps), c = 4 * stage_b_nq(g, t);
+    if constexpr (VEC) {
+      const bool ok = (k < krows) && (col0 + c < p.N);
+      s.b[ps] = buffer_load4(rb, ok ? (k * ldb + c) * 4 : kMaskedOffset);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool ok = (k < krows) && (col0 + c + e < p.N);
+        s.b[ps][e] = buffer_load1(rb, ok ? (k * ldb + c + e) * 4 : kMaskedOffset);
+      }
+    }
+  }
+}
+
+// Registers -> LDS stage: A scattered transposed into As[k][m], B as float4
+// rows of Bs[k][n].
+template <class Cfg>
+__device__ __forceinline__ void stage_store(float* stage, int t, const Staged<Cfg>& s) {
+  constexpr Geom g = make_geom(Cfg::tile);
+#pragma unroll
+  for (int ps = 0; ps < g.PASSES_A; ++ps) {
+    const int m = stage_a_row(g, t, ps), c = 4 * stage_a_kq(g, t);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) stage[as_index(g, c + e, m)] = s.a[ps][e];
+  }
+#pragma unroll
+  for (int ps = 0; ps < g.PASSES_B; ++ps) {
+    const int k = stage_b_row(g, t, ps), c = 4 * stage_b_nq(g, t);
+    *reinterpret_cast<f32x4*>(&stage[bs_index(g, k, c)]) = s.b[ps];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Accumulator storage and the inner product, per path.
+
+template <class Cfg, int PATH = Cfg::PATH>
+struct Acc;
+
+template <class Cfg>
+struct Acc<Cfg, kPathValu> {
+  float v[Cfg::WMITER * Cfg::TM * Cfg::WNITER * Cfg::TN];
+};
+
+template <class Cfg>
+struct Acc<Cfg, kPathMfma32> {
+  f32x16 v[Cfg::WMITER][Cfg::WNITER];
+};
+
+template <class Cfg>
+struct Acc<Cfg, kPathMfma16> {
+  f32x4 v[Cfg::WMITER][Cfg::WNITER];
+};
+
+template <class Cfg>
+__device__ __forceinline__ void acc_zero(Acc<Cfg>& acc) {
+  if constexpr (Cfg::PATH == kPathValu) {
+#pragma unroll
+    for (auto& x : acc.v) x = 0.0f;
+  } else {
+#pragma unroll
+    for (int i = 0; i < Cfg::WMITER; ++i)
+#pragma unroll
+      for (int j = 0; j < Cfg::WNITER; ++j) acc.v[i][j] = {};
+  }
+}
+
+// One BK slice of the inner product, reading LDS stage `st`.
+template <class Cfg>
+__device__ __forceinline__ void inner_product(const float* st, int wr0, int wc0, int lane,
+                                              Acc<Cfg>& acc) {
+  constexpr Geom g = make_geom(Cfg::tile);
+  if constexpr (Cfg::PATH == kPathValu) {
+    // Outer product of regM (WMITER*TM values down m) and regN (WNITER*TN
+    // values along n) per k, the page's third tiling level; 128-bit LDS reads.
+#pragma unroll
+    for (int k = 0; k < g.BK; ++k) {
+      float rm[g.WMITER * g.TM], rn[g.WNITER * g.TN];
+#pragma unroll
+      for (int wm = 0; wm < g.WMITER; ++wm)
+#pragma unroll
+        for (int i = 0; i < g.TM; i += 4) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(&st[as_index(g, k, wr0 + valu_m(g, lane, wm, i))]);
+          rm[wm * g.TM + i + 0] = v[0]; rm[wm * g.TM + i + 1] = v[1];
+          rm[wm * g.TM + i + 2] = v[2]; rm[wm * g.TM + i + 3] = v[3];
+        }
+#pragma unroll
+      for (int wn = 0; wn < g.WNITER; ++wn)
+#pragma unroll
+        for (int j = 0; j < g.TN; j += 4) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(&st[bs_index(g, k, wc0 + valu_n(g, lane, wn, j))]);
+          rn[wn * g.TN + j + 0] = v[0]; rn[wn * g.TN + j + 1] = v[1];
+          rn[wn * g.TN + j + 2] = v[2]; rn[wn * g.TN + j + 3] = v[3];
+        }
+#pragma unroll
+      for (int wm = 0; wm < g.WMITER; ++wm)
+#pragma unroll
+        for (int i = 0; i < g.TM; ++i)
+#pragma unroll
+          for (int wn = 0; wn < g.WNITER; ++wn)
+#pragma unroll
+            for (int j = 0; j < g.TN; ++j) {
+              float& a = acc.v[valu_acc_index(g, wm, i, wn, j)];
+              a = __builtin_fmaf(rm[wm * g.TM + i], rn[wn * g.TN + j], a);
+            }
+    }
+  } else {
+    constexpr int blk = mfma_blk(g), kstep = mfma_kstep(g);
+    const int fr = mfma_frag_row(g, lane), slot = mfma_frag_slot(g, lane);
+#pragma unroll
+    for (int kk = 0; kk < g.BK; kk += kstep) {
+      const int k = kk + slot;
+      float a[g.WMITER], b[g.WNITER];
+#pragma unroll
+      for (int wm = 0; wm < g.WMITER; ++wm) a[wm] = st[as_index(g, k, wr0 + wm * blk + fr)];
+#pragma unroll
+      for (int wn = 0; wn < g.WNITER; ++wn) b[wn] = st[bs_index(g, k, wc0 + wn * blk + fr)];
+#pragma unroll
+      for (int wm = 0; wm < g.WMITER; ++wm)
+#pragma unroll
+        for (int wn = 0; wn < g.WNITER; ++wn) {
+          if constexpr (Cfg::PATH == kPathMfma32)
+            acc.v[wm][wn] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[wm], b[wn], acc.v[wm][wn], 0, 0, 0);
+          else
+            acc.v[wm][wn] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[wm], b[wn], acc.v[wm][wn], 0, 0, 0);
+        }
+    }
+  }
+}
+
+__device__ __forceinline__ void update_one(float* c, float acc, float alpha, float beta) {
+  float v = alpha * acc;
+  if (beta != 0.0f) v = __builtin_fmaf(beta, *c, v);
+  *c = v;
+}
+
+// C = alpha*acc + beta*C for in-range elements.  When beta == 0 the old C is
+// not read.  `cw` points at C[row0 + wr0][col0 + wc0]; rlim/clim are the rows
+// and columns of the wave tile that lie inside M x N.
+template <class Cfg, bool VEC>
+__device__ __forceinline__ void epilogue(float* cw, int ldc, int rlim, int clim, int lane,
+                                         float alpha, float beta, const Acc<Cfg>& acc) {
+  constexpr Geom g = make_geom(Cfg::tile);
+  if constexpr (Cfg::PATH == kPathValu) {
+#pragma unroll
+    for (int wm = 0; wm < g.WMITER; ++wm)
+#pragma unroll
+      for (int i = 0; i < g.TM; ++i) {
+        const int r = valu_m(g, lane, wm, i);
+        if (r >= rlim) continue;
+#pragma unroll
+        for (int wn = 0; wn < g.WNITER; ++wn)
+#pragma unroll
+          for (int j = 0; j < g.TN; j += 4) {
+            const int c = valu_n(g, lane, wn, j);
+            float* cp = cw + r * ldc + c;
+            const int e = valu_acc_index(g, wm, i, wn, j);
+            if constexpr (VEC) {
+              if (c < clim) {  // N % 4 == 0: the float4 is wholly inside or outside
+                f32x4 v = {alpha * acc.v[e], alpha * acc.v[e + 1], alpha * acc.v[e + 2],
+                           alpha * acc.v[e + 3]};
+                if (beta != 0.0f) {
+                  const f32x4 old = *reinterpret_cast<const f32x4*>(cp);
+#pragma unroll
+                  for (int q = 0; q < 4; ++q) v[q] = __builtin_fmaf(beta, old[q], v[q]);
+                }
+                *reinterpret_cast<f32x4*>(cp) = v;
+              }
+            } else {
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                if (c + q < clim) update_one(cp + q, acc.v[e + q], alpha, beta);
+            }
+          }
+      }
+  } else {
+    constexpr int blk = mfma_blk(g), regs = mfma_regs(g);
+    const int c_l = mfma_out_col(g, lane);
+#pragma unroll
+    for (int wm = 0; wm < g.WMITER; ++wm)
+#pragma unroll
+      for (int wn = 0; wn < g.WNITER; ++wn) {
+        const int c = wn * blk + c_l;
+        if (c >= clim) continue;
+#pragma unroll
+        for (int r = 0; r < regs; ++r) {
+          const int row = wm * blk + mfma_out_row(g, lane, r);
+          if (row < rlim) update_one(cw + row * ldc + c, acc.v[wm][wn][r], alpha, beta);
+        }
+      }
+  }
+}
+
+template <class Cfg, bool VEC>
+__global__ void __launch_bounds__(Cfg::NT) sgemm_tile_kernel(KernelArgs p) {
+  constexpr Geom g = make_geom(Cfg::tile);
+  static_assert(tile_legal(Cfg::tile), "illegal tile tuple instantiated");
+  __shared__ __attribute__((aligned(16))) float lds[2 * g.STAGE];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int tile = blockIdx.x;
+  const int row0 = (tile / p.tiles_n) * g.BM;
+  const int col0 = (tile % p.tiles_n) * g.BN;
+  const int wr0 = wave_row0(g, wave), wc0 = wave_col0(g, wave);
+
+  Acc<Cfg> acc;
+  acc_zero(acc);
+  Staged<Cfg> s;
+
+  const int nk = (p.K + g.BK - 1) / g.BK;
+  stage_load<Cfg, VEC>(p, row0, col0, 0, t, s);
+  stage_store<Cfg>(lds, t, s);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const float* cur = lds + (kt & 1) * g.STAGE;
+    const bool more = kt + 1 < nk;
+    if (more) stage_load<Cfg, VEC>(p, row0, col0, (kt + 1) * g.BK, t, s);
+    inner_product<Cfg>(cur, wr0, wc0, lane, acc);
+    if (more) stage_store<Cfg>(lds + ((kt + 1) & 1) * g.STAGE, t, s);
+    __syncthreads();
+  }
+
+  const int rlim = min(g.WM, p.M - row0 - wr0);
+  const int clim = min(g.WN, p.N - col0 - wc0);
+  if (rlim <= 0 || clim <= 0) return;
+  float* cw = p.C + static_cast<long long>(row0 + wr0) * p.ldc + (col0 + wc0);
+  epilogue<Cfg, VEC>(cw, static_cast<int>(p.ldc), rlim, clim, lane, p.alpha, p.beta, acc);
+}
+
+// Host-side launcher for one instantiated tuple and variant.
+template <class Cfg, bool VEC>
+hipError_t launch_tile(const KernelArgs& a, hipStream_t stream) {
+  KernelArgs k = a;
+  const long long tiles_m = (a.M + Cfg::BM - 1) / Cfg::BM;
+  const long long tiles_n = (a.N + Cfg::BN - 1) / Cfg::BN;
+  k.tiles_n = static_cast<int>(tiles_n);
+  void* args[] = {&k};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&sgemm_tile_kernel<Cfg, VEC>),
+                         dim3(static_cast<unsigned>(tiles_m * tiles_n)), dim3(Cfg::NT), args, 0,
+                         stream);
+}
+
+template <class Cfg, bool VEC>
+const void* kernel_symbol() {
+  return reinterpret_cast<const void*>(&sgemm_tile_kernel<Cfg, VEC>);
+}
+
+}  // namespace fp32gemm

@@ -1,0 +1,226 @@
+// tile_config.hpp -- the tile tuple, its derived quantities, and the
+// compile-time legality checker for the SGEMM kernels.
+//
+// The tuple is the nine-number parameter list of the warp-tiled kernel on
+// "Warp Tiling: A Third Level of Tiling" (section "The Kernel": BM, BN, BK,
+// WM, WN, WNITER, TM, TN, NUM_THREADS, with WMITER derived), plus a path tag:
+//
+//   VALU    : each lane owns WMITER x WNITER patches of TM x TN outputs and
+//             forms them as outer products with scalar FMAs.
+//   MFMA32  : each WSUBM x WSUBN = 32 x 32 sub-tile is one accumulator block of
+//             v_mfma_f32_32x32x2_f32; a lane's share of it is 16 outputs, so the
+//             tuple carries TM x TN = 16 x 1.
+//   MFMA16  : 16 x 16 sub-tiles of v_mfma_f32_16x16x4_f32; TM x TN = 4 x 1.
+//
+// The checker restates, for a 64-lane wave, the assumptions the page
+// "Autotuning: Searching the Tile-Shape Space" (section "Most Configurations
+// Are Not Wrong By A Little") lists for the kernel body: whole waves, whole
+// warp tiles, an integral WMITER, exact sub-tile coverage, 4-element vector
+// alignment, load loops that tile the staged blocks exactly, single ownership
+// of each output, and the shared-memory and accumulator limits.  The guards
+// are ordered so that no guard divides by a quantity an earlier guard has not
+// already shown to be positive.  On top of those it enforces what the gfx950
+// kernels in this library assume: double-buffered LDS within the per-workgroup
+// limit, the XOR swizzle's range, the MFMA block shapes and k-step, and an
+// estimated register budget.
+//
+// Everything here is constexpr and free of HIP types, so the same functions
+// gate template instantiation (with `if constexpr`), run on the host for the
+// tests and the tuner, and feed the index-map simulator.
+#pragma once
+
+namespace fp32gemm {
+
+enum Path : int { kPathValu = 0, kPathMfma32 = 1, kPathMfma16 = 2 };
+
+struct Tile {
+  int BM, BN, BK, WM, WN, WNITER, TM, TN, NT, path;
+  int swz;  // LDS bank count the As/Bs XOR swizzle is built for: 0 (none), 32 or 64
+};
+
+// Machine limits the checker enforces.
+struct Target {
+  int wave;           // lanes per wave (warp)
+  int lds_bytes;      // shared memory available to one workgroup
+  int lds_buffers;    // 1 = single-buffered tiles, 2 = double-buffered
+  int max_acc;        // accumulators one lane may hold
+  int max_arch_vgpr;  // architectural VGPRs per lane (VALU operands)
+  int max_vgpr;       // VGPR + AccVGPR per lane
+  bool allow_mfma;
+  bool gfx950_rules;  // swizzle range, vector reads of As, register estimate
+};
+
+// MI355X (gfx950): wave64, 160 KiB LDS per workgroup, double buffering,
+// 256 architectural VGPRs + 256 AccVGPRs per lane.
+constexpr Target kGfx950{64, 160 * 1024, 2, 256, 256, 512, true, true};
+
+// The page's own machine model: 32-lane warps, 48 KB of static shared memory,
+// single-buffered tiles, at most 128 accumulators per thread.
+constexpr Target kPageModel{32, 48 * 1024, 1, 128, 1 << 30, 1 << 30, false, false};
+
+// Reason codes, one per guard, in evaluation order.
+enum Reason : int {
+  kLegal = 0,
+  kBadRange = 1,            // a parameter is non-positive, or too many threads
+  kThreadsNotWaves = 2,     // NT is not a whole number of waves
+  kBlockNotWarpTiled = 3,   // BM % WM or BN % WN
+  kWarpCount = 4,           // warp tiles != waves
+  kWmiterFraction = 5,      // WM*WN not divisible by wave*TM*TN*WNITER
+  kSubtileSplit = 6,        // WMITER < 1, WM % WMITER or WN % WNITER
+  kLaneTile = 7,            // WSUBM % TM or WSUBN % TN
+  kSubtileLanes = 8,        // lanes per sub-tile != wave
+  kVectorAlign = 9,         // BK, BN, TN (and on gfx950 BM, TM) not multiples of 4
+  kLoadStrideA = 10,        // A staging loop does not tile BM x BK exactly
+  kLoadStrideB = 11,        // B staging loop does not tile BK x BN exactly
+  kOwnership = 12,          // threads x outputs/thread != BM*BN
+  kLdsOverflow = 13,        // staged tiles exceed the LDS budget
+  kAccOverflow = 14,        // accumulators per lane over the limit
+  kMfmaShape = 15,          // MFMA sub-tile / lane tile / k-step mismatch
+  kSwizzleRange = 16,       // swizzle needs BM, BN multiples of swz, BK <= swz, BK/4 a power of 2
+  kRegisterEstimate = 17,   // estimated registers over the per-lane budget
+  kNoMfmaOnTarget = 18,
+  kNumReasons = 19,
+};
+
+constexpr int wmiter_of(const Tile& t, int wave) {
+  return (t.WM * t.WN) / (wave * t.TM * t.TN * t.WNITER);
+}
+
+// Accumulators per lane.
+constexpr int acc_per_lane(const Tile& t, int wave) {
+  return wmiter_of(t, wave) * t.TM * t.WNITER * t.TN;
+}
+
+// Floats per staged A tile row (As is [BK][SA], transposed) and B tile row
+// (Bs is [BK][SB]).  The swizzle permutes within a row, so no padding.
+constexpr int lds_stride_a(const Tile& t) { return t.BM; }
+constexpr int lds_stride_b(const Tile& t) { return t.BN; }
+
+constexpr int lds_floats_per_stage(const Tile& t) {
+  return t.BK * lds_stride_a(t) + t.BK * lds_stride_b(t);
+}
+
+constexpr int lds_bytes(const Tile& t, const Target& m) {
+  return m.lds_buffers * lds_floats_per_stage(t) * 4;
+}
+
+// Registers that hold one staged tile between its global load and its LDS
+// store (per lane).
+constexpr int prefetch_regs(const Tile& t) { return (t.BM * t.BK + t.BK * t.BN) / t.NT; }
+
+// A deliberately rough per-lane register estimate; the compiler's resource
+// report is the ground truth and spilling builds are rejected after compile.
+constexpr int vgpr_estimate(const Tile& t, int wave) {
+  const int wmiter = wmiter_of(t, wave);
+  const int fixed = 28;  // addresses, loop state, masks, alpha/beta
+  if (t.path == kPathValu) {
+    const int frags = 2 * (wmiter * t.TM + t.WNITER * t.TN);
+    return acc_per_lane(t, wave) + frags + prefetch_regs(t) + fixed;
+  }
+  // MFMA: fragments are one register per (sub-tile row or column, k-step);
+  // accumulators live in AccVGPRs.
+  const int ksteps = (t.path == kPathMfma32) ? 2 : 1;
+  return 2 * ksteps * (wmiter + t.WNITER) + prefetch_regs(t) + fixed;
+}
+
+constexpr int check_tile(const Tile& t, const Target& m) {
+  if (t.BM <= 0 || t.BN <= 0 || t.BK <= 0 || t.WM <= 0 || t.WN <= 0 || t.WNITER <= 0 ||
+      t.TM <= 0 || t.TN <= 0 || t.NT <= 0 || t.NT > 1024)
+    return kBadRange;
+  if (t.path != kPathValu && !m.allow_mfma) return kNoMfmaOnTarget;
+
+  // Whole waves, tiled evenly by warp tiles.
+  if (t.NT % m.wave != 0) return kThreadsNotWaves;
+  if (t.BM % t.WM != 0 || t.BN % t.WN != 0) return kBlockNotWarpTiled;
+  if ((t.BM / t.WM) * (t.BN / t.WN) != t.NT / m.wave) return kWarpCount;
+
+  // The warp tile splits into whole WMITER x WNITER sub-tiles.
+  const int denom = m.wave * t.TM * t.TN * t.WNITER;
+  if ((t.WM * t.WN) % denom != 0) return kWmiterFraction;
+  const int wmiter = (t.WM * t.WN) / denom;
+  if (wmiter < 1 || t.WM % wmiter != 0 || t.WN % t.WNITER != 0) return kSubtileSplit;
+
+  // Each sub-tile is covered by exactly one wave's lanes.
+  const int wsubm = t.WM / wmiter, wsubn = t.WN / t.WNITER;
+  if (wsubm % t.TM != 0 || wsubn % t.TN != 0) return kLaneTile;
+  if ((wsubm / t.TM) * (wsubn / t.TN) != m.wave) return kSubtileLanes;
+
+  // 4-wide vector accesses: global A rows along k, B rows along n, the C
+  // epilogue along n; on gfx950 also 128-bit reads of As along m.
+  if (t.BK % 4 != 0 || t.BN % 4 != 0) return kVectorAlign;
+  if (t.path == kPathValu && t.TN % 4 != 0) return kVectorAlign;
+  if (m.gfx950_rules && (t.BM % 4 != 0 || (t.path == kPathValu && t.TM % 4 != 0)))
+    return kVectorAlign;
+
+  // Staging loops: every thread loads one float4 per pass; the passes tile
+  // the BM x BK block of A and the BK x BN block of B with no remainder.
+  if ((t.NT * 4) % t.BK != 0) return kLoadStrideA;
+  const int row_stride_a = (t.NT * 4) / t.BK;
+  if (row_stride_a < 1 || t.BM % row_stride_a != 0) return kLoadStrideA;
+  if (t.NT % (t.BN / 4) != 0) return kLoadStrideB;
+  const int row_stride_b = t.NT / (t.BN / 4);
+  if (row_stride_b < 1 || t.BK % row_stride_b != 0) return kLoadStrideB;
+
+  // Every output element belongs to exactly one lane.
+  if (static_cast<long long>(t.NT) * wmiter * t.TM * t.WNITER * t.TN !=
+      static_cast<long long>(t.BM) * t.BN)
+    return kOwnership;
+
+  if (t.path == kPathMfma32 || t.path == kPathMfma16) {
+    const int blk = (t.path == kPathMfma32) ? 32 : 16;
+    const int tm = (t.path == kPathMfma32) ? 16 : 4;
+    const int kstep = (t.path == kPathMfma32) ? 2 : 4;
+    if (wsubm != blk || wsubn != blk || t.TM != tm || t.TN != 1 || t.BK % kstep != 0)
+      return kMfmaShape;
+  }
+
+  if (m.gfx950_rules) {
+    // The As/Bs XOR swizzle flips bits below swz, in steps of at least 4
+    // words, so it needs swz-aligned rows and at most swz/4 groups of four
+    // k-rows per staged tile.
+    if (t.swz != 0 && t.swz != 32 && t.swz != 64) return kSwizzleRange;
+    if (t.swz != 0 && (t.BM % t.swz != 0 || t.BN % t.swz != 0 || t.BK > t.swz ||
+                       ((t.BK / 4) & (t.BK / 4 - 1)) != 0))
+      return kSwizzleRange;
+  }
+
+  if (lds_bytes(t, m) > m.lds_bytes) return kLdsOverflow;
+  const int acc_limit = (t.path == kPathValu) ? (m.max_acc < 128 ? m.max_acc : 128) : m.max_acc;
+  if (acc_per_lane(t, m.wave) > acc_limit) return kAccOverflow;
+
+  if (m.gfx950_rules) {
+    const int est = vgpr_estimate(t, m.wave);
+    if (t.path == kPathValu) {
+      if (est > m.max_arch_vgpr) return kRegisterEstimate;
+    } else {
+      if (est > m.max_arch_vgpr || est + acc_per_lane(t, m.wave) > m.max_vgpr)
+        return kRegisterEstimate;
+    }
+  }
+  return kLegal;
+}
+
+constexpr bool tile_legal(const Tile& t) { return check_tile(t, kGfx950) == kLegal; }
+
+// Compile-time view of a legal tuple with its derived constants.
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int WNITER_, int TM_, int TN_, int NT_,
+          int PATH_, int SWZ_>
+struct TileCfg {
+  static constexpr Tile tile{BM_, BN_, BK_, WM_, WN_, WNITER_, TM_, TN_, NT_, PATH_, SWZ_};
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, WNITER = WNITER_;
+  static constexpr int TM = TM_, TN = TN_, NT = NT_, PATH = PATH_;
+  static constexpr int WAVE = 64;
+  static constexpr int WMITER = wmiter_of(tile, WAVE);
+  static constexpr int WSUBM = WM / WMITER, WSUBN = WN / WNITER;
+  static constexpr int WAVES_N = BN / WN;  // warp tiles across the block tile
+  static constexpr int KQ = BK / 4;        // float4 columns in a staged A row
+  static constexpr int NQ = BN / 4;        // float4 columns in a staged B row
+  static constexpr int ROWS_A = NT / KQ;   // A rows staged per pass
+  static constexpr int PASSES_A = BM / ROWS_A;
+  static constexpr int ROWS_B = NT / NQ;   // B rows staged per pass
+  static constexpr int PASSES_B = BK / ROWS_B;
+  static constexpr int SA = lds_stride_a(tile), SB = lds_stride_b(tile);
+  static constexpr int STAGE_FLOATS = lds_floats_per_stage(tile);
+};
+
+}  // namespace fp32gemm

@@ -1,0 +1,155 @@
+// tile_maps.hpp -- every index map the SGEMM kernels use, as constexpr
+// functions of a Geom (the tuple plus its derived constants).
+//
+// The kernels call these with a constexpr Geom, so they fold to constants;
+// the host simulator calls the very same functions with runtime Geoms and
+// checks, for every tuple, that outputs are owned exactly once, that the
+// staging loops cover each tile exactly once, that every LDS access stays in
+// its stage and is vector-aligned, and that each lane's fragment reads return
+// the (row, k) and (k, col) elements its accumulators need.
+//
+// Levels follow "Warp Tiling: A Third Level of Tiling" (section "The Kernel"
+// and its "Mechanics" list): block tile -> warp (here: wave64) tile ->
+// WMITER x WNITER interleaved sub-tiles -> lane patch.
+//
+// LDS layout.  As holds the A tile transposed, As[k][m] (the page "Vectorized
+// Memory Access: 128-bit Loads and Stores", section "Why As Has To Be
+// Transposed"), so a lane's consecutive m values sit next to each other.
+// Bs holds Bs[k][n] unchanged.  Rows are XOR-swizzled instead of padded.
+// With a row stride that is a multiple of the bank count, the transposed
+// store of a float4 of A puts every lane of one store phase into the bank
+// given by its row m alone -- the conflict that page's section "What Could Be
+// Improved" derives, and that grows with BK.  The swizzle, built for a bank
+// count NB (the tuple's swz, 32 or 64), XORs m with
+//   (k/4 mod KQ) * (NB/KQ)      so the KQ = BK/4 k-groups of one store phase
+//                               land on disjoint bank ranges, and
+//   a k-parity term (swz_rows)  so the consecutive k-rows that one MFMA
+//                               fragment read spreads over its lanes (2 rows
+//                               for 32x32x2, 4 for 16x16x4) land on disjoint
+//                               bank groups.
+// Both terms are multiples of 4 below NB, so aligned float4 groups stay
+// contiguous and every row keeps its NB-aligned blocks; Bs gets the second
+// term only (its store is a plain row-contiguous float4).
+#pragma once
+
+#include "tile_config.hpp"
+
+#if defined(__HIPCC__)
+#define FG_HD __host__ __device__
+#else
+#define FG_HD
+#endif
+
+namespace fp32gemm {
+
+struct Geom {
+  int BM, BN, BK, WM, WN, WNITER, TM, TN, NT, path, swz;
+  int wave, WMITER, WSUBM, WSUBN, WAVES_N, KQ, NQ, ROWS_A, PASSES_A, ROWS_B, PASSES_B;
+  int SA, SB, STAGE, ACC;
+};
+
+constexpr Geom make_geom(const Tile& t) {
+  Geom g{};
+  g.BM = t.BM; g.BN = t.BN; g.BK = t.BK; g.WM = t.WM; g.WN = t.WN; g.WNITER = t.WNITER;
+  g.TM = t.TM; g.TN = t.TN; g.NT = t.NT; g.path = t.path; g.swz = t.swz;
+  g.wave = 64;
+  g.WMITER = wmiter_of(t, 64);
+  g.WSUBM = t.WM / g.WMITER;
+  g.WSUBN = t.WN / t.WNITER;
+  g.WAVES_N = t.BN / t.WN;
+  g.KQ = t.BK / 4;
+  g.NQ = t.BN / 4;
+  g.ROWS_A = t.NT / g.KQ;
+  g.PASSES_A = t.BM / g.ROWS_A;
+  g.ROWS_B = t.NT / g.NQ;
+  g.PASSES_B = t.BK / g.ROWS_B;
+  g.SA = lds_stride_a(t);
+  g.SB = lds_stride_b(t);
+  g.STAGE = lds_floats_per_stage(t);
+  g.ACC = acc_per_lane(t, 64);
+  return g;
+}
+
+// ---- staging: global -> registers -> LDS --------------------------------
+// Pass p of thread t loads the float4 A[m][4*kq .. 4*kq+3] of the BM x BK
+// block: consecutive threads walk k first, so a row's BK floats are read by
+// KQ neighbouring lanes (coalesced along A's contiguous dimension).
+FG_HD constexpr int stage_a_row(const Geom& g, int t, int p) { return t / g.KQ + p * g.ROWS_A; }
+FG_HD constexpr int stage_a_kq(const Geom& g, int t) { return t % g.KQ; }
+// Pass p of thread t loads the float4 B[k][4*nq .. 4*nq+3] of the BK x BN block.
+FG_HD constexpr int stage_b_row(const Geom& g, int t, int p) { return t / g.NQ + p * g.ROWS_B; }
+FG_HD constexpr int stage_b_nq(const Geom& g, int t) { return t % g.NQ; }
+
+// ---- LDS addresses (floats, relative to one stage) ------------------------
+FG_HD constexpr int swz_rows(const Geom& g, int k) {
+  // 32 banks: consecutive k-rows differ in bit 4.  64 banks: k-row pairs
+  // differ in bit 5 (the two slots of a 32x32x2 fragment read fill both
+  // 32-bank halves) and bit 4 separates the pairs (four distinct 16-bank
+  // groups for the four slots of a 16x16x4 read).
+  return g.swz == 32 ? ((k & 1) << 4) : g.swz == 64 ? (((k & 1) << 5) | ((k & 2) << 3)) : 0;
+}
+FG_HD constexpr int swz_a(const Geom& g, int k) {
+  return g.swz == 0 ? 0 : ((((k >> 2) % g.KQ) * (g.swz / g.KQ)) ^ swz_rows(g, k));
+}
+FG_HD constexpr int swz_b(const Geom& g, int k) { return swz_rows(g, k); }
+FG_HD constexpr int as_index(const Geom& g, int k, int m) { return k * g.SA + (m ^ swz_a(g, k)); }
+FG_HD constexpr int bs_index(const Geom& g, int k, int n) {
+  return g.BK * g.SA + k * g.SB + (n ^ swz_b(g, k));
+}
+
+// ---- waves inside the block tile -----------------------------------------
+FG_HD constexpr int wave_row0(const Geom& g, int w) { return (w / g.WAVES_N) * g.WM; }
+FG_HD constexpr int wave_col0(const Geom& g, int w) { return (w % g.WAVES_N) * g.WN; }
+
+// ---- VALU path: lanes inside one WSUBM x WSUBN sub-tile ---------------------
+// The 64 lanes form a (WSUBM/TM) x (WSUBN/TN) grid of TM x TN patches.
+FG_HD constexpr int valu_lane_row(const Geom& g, int l) { return l / (g.WSUBN / g.TN); }
+FG_HD constexpr int valu_lane_col(const Geom& g, int l) { return l % (g.WSUBN / g.TN); }
+// Row (within the wave tile) of regM entry wm*TM + i, and column of regN entry wn*TN + j.
+FG_HD constexpr int valu_m(const Geom& g, int l, int wm, int i) {
+  return wm * g.WSUBM + valu_lane_row(g, l) * g.TM + i;
+}
+FG_HD constexpr int valu_n(const Geom& g, int l, int wn, int j) {
+  return wn * g.WSUBN + valu_lane_col(g, l) * g.TN + j;
+}
+// Accumulator e = (wm*TM + i) * (WNITER*TN) + wn*TN + j.
+FG_HD constexpr int valu_acc_index(const Geom& g, int wm, int i, int wn, int j) {
+  return (wm * g.TM + i) * (g.WNITER * g.TN) + wn * g.TN + j;
+}
+
+// ---- MFMA paths ------------------------------------------------------------
+// v_mfma_f32_32x32x2_f32: lane l supplies A[i = l%32][s = l/32] and
+// B[s = l/32][j = l%32]; accumulator register r of lane l is
+// D[8*(r/4) + 4*(l/32) + r%4][l%32].
+// v_mfma_f32_16x16x4_f32: lane l supplies A[l%16][l/16] and B[l/16][l%16];
+// register r of lane l is D[4*(l/16) + r][l%16].
+// Slot s of the k-step starting at kk reads k-row kk + s.
+FG_HD constexpr int mfma_blk(const Geom& g) { return g.path == kPathMfma32 ? 32 : 16; }
+FG_HD constexpr int mfma_kstep(const Geom& g) { return g.path == kPathMfma32 ? 2 : 4; }
+FG_HD constexpr int mfma_regs(const Geom& g) { return g.path == kPathMfma32 ? 16 : 4; }
+FG_HD constexpr int mfma_frag_row(const Geom& g, int l) { return l % mfma_blk(g); }
+FG_HD constexpr int mfma_frag_slot(const Geom& g, int l) { return l / mfma_blk(g); }
+FG_HD constexpr int mfma_out_row(const Geom& g, int l, int r) {
+  return g.path == kPathMfma32 ? 8 * (r / 4) + 4 * (l / 32) + (r % 4) : 4 * (l / 16) + r;
+}
+FG_HD constexpr int mfma_out_col(const Geom& g, int l) { return l % mfma_blk(g); }
+
+// ---- output ownership (row, col within the block tile) ---------------------
+// Accumulator e of lane l in wave w.
+struct RC { int r, c; };
+FG_HD constexpr RC owner(const Geom& g, int w, int l, int e) {
+  if (g.path == kPathValu) {
+    const int row_in = e / (g.WNITER * g.TN);  // wm*TM + i
+    const int col_in = e % (g.WNITER * g.TN);  // wn*TN + j
+    const int wm = row_in / g.TM, i = row_in % g.TM;
+    const int wn = col_in / g.TN, j = col_in % g.TN;
+    return RC{wave_row0(g, w) + valu_m(g, l, wm, i), wave_col0(g, w) + valu_n(g, l, wn, j)};
+  }
+  const int regs = mfma_regs(g), blk = mfma_blk(g);
+  const int sub = e / regs, r = e % regs;
+  const int wm = sub / g.WNITER, wn = sub % g.WNITER;
+  return RC{wave_row0(g, w) + wm * blk + mfma_out_row(g, l, r),
+            wave_col0(g, w) + wn * blk + mfma_out_col(g, l)};
+}
+
+}  // namespace fp32gemm

@@ -1,0 +1,137 @@
+"""The C ABI on the CPU: the library loads, exports every function the header
+declares, and validates arguments before touching any device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import fp32_gemm_amd as fg
+from fp32_gemm_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp32_gemm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(sgemm\w*)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_expected_api():
+    names = declared_functions()
+    assert "sgemm" in names and "sgemm_ex" in names
+    assert names == binding.exported_symbols()
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(fg.library_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", fg.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (sgemm\w*)$", out, flags=re.M))
+    assert set(declared_functions()) <= exported
+
+
+FAKE = 1 << 40  # a well-aligned, never-dereferenced address
+
+
+def plan(M, N, K, lda, ldb, ldc, A=FAKE, B=FAKE * 2, C=FAKE * 4, cfg=-1):
+    try:
+        return 0, binding.plan(M, N, K, A, lda, B, ldb, C, ldc, cfg)
+    except fg.SgemmError as e:
+        return e.status, None
+
+
+@pytest.mark.parametrize("args,code", [
+    ((-1, 4, 4, 4, 4, 4), -1),
+    ((4, -1, 4, 4, 4, 4), -2),
+    ((4, 4, -1, 4, 4, 4), -3),
+    ((4, 4, 8, 7, 4, 4), -6),
+    ((4, 8, 4, 4, 7, 8), -8),
+    ((4, 8, 4, 4, 8, 7), -11),
+    ((4, 4, 4, 1 << 21, 4, 4), 5),
+    ((2 ** 30 + 1, 4, 4, 4, 4, 4), 5),
+])
+def test_argument_codes(args, code):
+    assert plan(*args)[0] == code
+
+
+def test_null_pointers():
+    assert plan(4, 4, 4, 4, 4, 4, A=None)[0] == -5
+    assert plan(4, 4, 4, 4, 4, 4, B=None)[0] == -7
+    assert plan(4, 4, 4, 4, 4, 4, C=None)[0] == -10
+    # Empty operands may be NULL.
+    assert plan(4, 4, 0, 1, 4, 4, A=None, B=None)[0] == 0
+    assert plan(0, 0, 4, 4, 1, 1, A=None, B=FAKE, C=None)[0] == 0
+
+
+def test_overlap_is_rejected():
+    # C's extent starts inside A's extent.
+    assert plan(64, 64, 64, 64, 64, 64, A=FAKE, B=FAKE * 2, C=FAKE + 1024)[0] == 3
+    assert plan(64, 64, 64, 64, 64, 64, A=FAKE, B=FAKE * 2, C=FAKE * 2 + 64)[0] == 3
+    # Adjacent but disjoint.
+    assert plan(64, 64, 64, 64, 64, 64, A=FAKE, B=FAKE * 2, C=FAKE + 64 * 64 * 4)[0] == 0
+
+
+def test_variant_selection():
+    code, p = plan(256, 256, 256, 256, 256, 256)
+    assert code == 0 and p["vector_variant"] == 1
+    assert plan(256, 256, 255, 255, 256, 256)[1]["vector_variant"] == 0   # K % 4
+    assert plan(256, 255, 256, 256, 255, 255)[1]["vector_variant"] == 0   # N % 4
+    assert plan(256, 256, 256, 260, 256, 258)[1]["vector_variant"] == 0   # ldc % 4
+    assert plan(256, 256, 256, 256, 256, 256, A=FAKE + 4)[1]["vector_variant"] == 0  # alignment
+
+
+def test_bad_config_id():
+    assert plan(4, 4, 4, 4, 4, 4, cfg=fg.num_configs())[0] == 2
+    with pytest.raises(fg.SgemmError):
+        fg.config_info(-1)
+
+
+def test_tuned_dispatch_picks_a_compiled_config():
+    for M, N, K in [(4096, 4096, 4096), (256, 256, 256), (1000, 1500, 777), (8192, 2048, 4096),
+                    (1, 1, 1), (4097, 4095, 4093)]:
+        code, p = plan(M, N, K, K, N, N)
+        assert code == 0
+        info = fg.config_info(p["cfg_id"])
+        assert p["block"] == info["NT"]
+        assert p["grid"] == -(-M // info["BM"]) * -(-N // info["BN"])
+
+
+def test_quick_return_and_no_device():
+    # M == 0: nothing to do, success without a device.
+    assert binding.sgemm_raw(0, 4, 4, 1.0, FAKE, 4, FAKE * 2, 4, 0.0, FAKE * 4, 4) == 0
+    import torch
+    if not torch.cuda.is_available():
+        assert binding.sgemm_raw(4, 4, 4, 1.0, FAKE, 4, FAKE * 2, 4, 0.0, FAKE * 4, 4) == 1
+        assert fg.device_check() == 1
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -5, -6, -7, -8, -10, -11, 1, 2, 3, 4, 5):
+        s = fg.status_string(code)
+        assert s and s != "unknown status"
+    assert fg.status_string(12345) == "unknown status"
+
+
+def test_config_table_contents():
+    cfgs = fg.configs()
+    paths = {c["path_name"] for c in cfgs}
+    assert paths == {"valu", "mfma32", "mfma16"}
+    for c in cfgs:
+        assert c["WMITER"] * c["WSUBM"] == c["WM"] and c["WNITER"] * c["WSUBN"] == c["WN"]
+        assert c["lds_bytes"] <= 160 * 1024
+        assert c["resources_vec"] is not None and c["resources_scalar"] is not None
+
+
+def test_default_configs_do_not_spill():
+    for M, N, K in [(4096, 4096, 4096), (256, 256, 256), (1024, 1024, 1024)]:
+        _, p = plan(M, N, K, K, N, N)
+        c = fg.config_info(p["cfg_id"])
+        res = [x for x in fg.configs() if x["id"] == c["id"]][0]
+        assert res["resources_vec"]["ScratchSize"] == 0
+        assert res["resources_scalar"]["ScratchSize"] == 0

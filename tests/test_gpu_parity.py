@@ -1,0 +1,324 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bar: max|C_gpu - C64| / (K * max|A| * max|B|) <= 1e-6, bit-exact equality on
+inputs whose sums are exact in fp32 (small integers, identity, all-ones,
+rank-1), and every byte of C outside the M x N window untouched.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from fp32_gemm_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-6
+CANARY = 0x7FC0DEAD  # a NaN payload no computation produces
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def fg(dev):
+    import fp32_gemm_amd
+    assert fp32_gemm_amd.device_check() == 0, "current device is not gfx950"
+    return fp32_gemm_amd
+
+
+@pytest.fixture(scope="module")
+def orc():
+    from oracle import oracle
+    oracle.build(force=False)
+    return oracle
+
+
+class Canvas:
+    """C placed inside a larger allocation: `guard` canary rows above and
+    below, and canary padding columns [N, ldc)."""
+
+    def __init__(self, C, ldc, guard, dev):
+        M, N = C.shape
+        self.M, self.N, self.guard = M, N, guard
+        self.big = torch.full((M + 2 * guard, ldc), CANARY, dtype=torch.int32, device=dev)
+        self.view = self.big.view(torch.float32)[guard:guard + M, :N]
+        self.view.copy_(torch.from_numpy(C))
+
+    def result(self):
+        return self.view.cpu().numpy()
+
+    def untouched(self):
+        b = self.big.cpu().numpy().copy()
+        b[self.guard:self.guard + self.M, :self.N] = CANARY
+        return bool(np.all(b == CANARY))
+
+
+def to_dev(x, dev):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+
+def check_close(got, C64, K, A, B, what):
+    err = _err(got, C64, K, A, B)
+    assert err is not None and err <= TOL, f"{what}: err={err}"
+    return err
+
+
+def _err(got, C64, K, A, B):
+    from oracle import oracle
+    den = (K, float(np.abs(A).max()) if A.size else 0.0, float(np.abs(B).max()) if B.size else 0.0)
+    return oracle.rel_error(got, C64, *den)
+
+
+# ---------------------------------------------------------------------------
+# Every compiled configuration, both variants, on a shape with ragged edges
+# in M, N and K (several tiles in each direction for every tile size).
+
+SHAPE_VEC = (600, 600, 100)     # K % 4 == N % 4 == 0: float4 variant
+SHAPE_SCALAR = (601, 599, 99)   # scalar variant
+
+
+@pytest.fixture(scope="module")
+def ragged_cases(orc):
+    cases = {}
+    for name, (M, N, K) in (("vec", SHAPE_VEC), ("scalar", SHAPE_SCALAR)):
+        A, B, C = inputs.make_random(M, N, K, seed=900 + M)
+        r32, r64 = orc.sgemm(A, B, C, 0.5, 3.0)
+        Ai, Bi, Ci = inputs.make_small_int(M, N, K, seed=901 + M)
+        i32, _ = orc.sgemm(Ai, Bi, Ci, 0.5, 3.0)
+        cases[name] = dict(shape=(M, N, K), rnd=(A, B, C, r64), ints=(Ai, Bi, Ci, i32))
+    return cases
+
+
+def run(fg, dev, A, B, C, alpha, beta, cfg=-1, ldc_pad=5, guard=3):
+    M, N = C.shape
+    cv = Canvas(C, N + ldc_pad, guard, dev)
+    fg.sgemm_ex(to_dev(A, dev), to_dev(B, dev), cv.view, alpha, beta, cfg_id=cfg)
+    torch.cuda.synchronize()
+    return cv
+
+
+CHUNKS = 12
+
+
+@pytest.mark.parametrize("chunk", range(CHUNKS))
+def test_every_config_both_variants(fg, dev, ragged_cases, chunk):
+    cfgs = [c for c in fg.configs() if c["id"] % CHUNKS == chunk]
+    log(f"[parity] chunk {chunk}: {len(cfgs)} configs x 2 variants")
+    worst = 0.0
+    for c in cfgs:
+        for variant in ("vec", "scalar"):
+            case = ragged_cases[variant]
+            M, N, K = case["shape"]
+            log(f"[parity] cfg {c['id']} {c['path_name']} {c['tuple']} {variant} {M}x{N}x{K}")
+            A, B, C, r64 = case["rnd"]
+            cv = run(fg, dev, A, B, C, 0.5, 3.0, cfg=c["id"], ldc_pad=4 if variant == "vec" else 5)
+            assert cv.untouched(), f"cfg {c['id']} {variant}: wrote outside C"
+            worst = max(worst, check_close(cv.result(), r64, K, A, B, f"cfg {c['id']} {variant}"))
+            Ai, Bi, Ci, i32 = case["ints"]
+            cv = run(fg, dev, Ai, Bi, Ci, 0.5, 3.0, cfg=c["id"], ldc_pad=4 if variant == "vec" else 5)
+            got = cv.result()
+            assert np.array_equal(got.view(np.uint32), i32.view(np.uint32)), \
+                f"cfg {c['id']} {variant}: integer inputs not bit-exact"
+    log(f"[parity] worst err {worst:.3e}")
+
+
+# ---------------------------------------------------------------------------
+# The workload configurations, through the tuned dispatch.
+
+FULL_ORACLE = {"sq256", "sq1024", "sq2048", "ragged1000x1500x777"}
+
+
+@pytest.mark.parametrize("name", list(inputs.WORKLOADS))
+def test_workload(fg, dev, orc, name):
+    w = inputs.WORKLOADS[name]
+    log(f"[workload] {name} {w.M}x{w.N}x{w.K} alpha={w.alpha} beta={w.beta}")
+    A, B, C = inputs.make(w)
+    cv = run(fg, dev, A, B, C, w.alpha, w.beta, ldc_pad=0, guard=2)
+    got = cv.result()
+    assert cv.untouched()
+    if name in FULL_ORACLE:
+        _, r64 = orc.sgemm(A, B, C, w.alpha, w.beta)
+        err = check_close(got, r64, w.K, A, B, name)
+    else:
+        rows, cols = inputs.sample_indices(w.M, w.N, 4000, seed=w.seed)
+        _, e64 = orc.entries(rows, cols, A, B, C, w.alpha, w.beta)
+        err = _err(got[rows, cols], e64, w.K, A, B)
+        assert err <= TOL, f"{name}: sampled err={err}"
+    log(f"[workload] {name} err={err:.3e}")
+
+
+@pytest.mark.parametrize("shape", [(4097, 4095, 4093), (1000, 1500, 777), (4096, 4096, 4096)])
+def test_integer_inputs_bit_exact_full_size(fg, dev, orc, shape):
+    M, N, K = shape
+    log(f"[int] {M}x{N}x{K}")
+    A, B, C = inputs.make_small_int(M, N, K, seed=77)
+    cv = run(fg, dev, A, B, C, 0.5, 3.0, ldc_pad=3, guard=1)
+    got = cv.result()
+    assert cv.untouched()
+    rows, cols = inputs.sample_indices(M, N, 3000, seed=78)
+    # Whole rows at the first, a middle and the last tile row, plus the samples.
+    for r in (0, M // 2, M - 1):
+        rows = np.concatenate([rows, np.full(N, r)])
+        cols = np.concatenate([cols, np.arange(N)])
+    e32, _ = orc.entries(rows, cols, A, B, C, 0.5, 3.0)
+    assert np.array_equal(got[rows, cols].view(np.uint32), e32.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# Closed forms at full size.
+
+@pytest.mark.parametrize("M,N", [(4096, 4096), (777, 1500)])
+def test_identity_gives_B(fg, dev, M, N):
+    K = M
+    B = inputs.make_random(1, N, K, seed=5)[1]
+    A = np.eye(M, dtype=np.float32)
+    cv = run(fg, dev, A, B, np.zeros((M, N), np.float32), 1.0, 0.0)
+    assert np.array_equal(cv.result().view(np.uint32), B.view(np.uint32))
+
+
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 4096), (4097, 4095, 4093), (8192, 2048, 4096)])
+def test_all_ones_gives_K(fg, dev, M, N, K):
+    A = torch.ones((M, K), dtype=torch.float32, device=dev)
+    B = torch.ones((K, N), dtype=torch.float32, device=dev)
+    C = torch.full((M, N), 2.0, dtype=torch.float32, device=dev)
+    fg.sgemm(A, B, C, 0.5, 3.0)
+    torch.cuda.synchronize()
+    assert torch.all(C == 0.5 * K + 6.0).item()
+
+
+def test_rank1_is_correctly_rounded(fg, dev):
+    M, N = 513, 257
+    rng = np.random.default_rng(3)
+    a = rng.uniform(-1, 1, (M, 1)).astype(np.float32)
+    b = rng.uniform(-1, 1, (1, N)).astype(np.float32)
+    for c in fg.configs():
+        cv = run(fg, dev, a, b, np.zeros((M, N), np.float32), 1.0, 0.0, cfg=c["id"])
+        assert np.array_equal(cv.result(), a * b), f"cfg {c['id']} {c['path_name']}"
+
+
+# ---------------------------------------------------------------------------
+# Edge cases.
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (1, 300, 7), (300, 1, 7), (5, 5, 1), (33, 65, 17),
+                                   (257, 129, 3), (64, 64, 64)])
+def test_tiny_and_thin(fg, dev, orc, M, N, K):
+    A, B, C = inputs.make_random(M, N, K, seed=M * 1000 + N + K)
+    _, r64 = orc.sgemm(A, B, C, 0.5, 3.0)
+    cv = run(fg, dev, A, B, C, 0.5, 3.0)
+    assert cv.untouched()
+    check_close(cv.result(), r64, K, A, B, f"{M}x{N}x{K}")
+
+
+def test_K_zero_scales_C(fg, dev):
+    C = inputs.make_random(70, 90, 1, seed=2)[2]
+    A = torch.empty((70, 0), dtype=torch.float32, device=dev)
+    B = torch.empty((0, 90), dtype=torch.float32, device=dev)
+    cv = Canvas(C, 95, 2, dev)
+    fg.sgemm(A, B, cv.view, 0.5, 3.0)
+    torch.cuda.synchronize()
+    assert cv.untouched()
+    assert np.array_equal(cv.result(), (3.0 * C.astype(np.float64)).astype(np.float32))
+
+
+def test_M_or_N_zero_touches_nothing(fg, dev):
+    big = torch.full((10, 10), CANARY, dtype=torch.int32, device=dev)
+    f = big.view(torch.float32)
+    A = torch.ones((0, 4), dtype=torch.float32, device=dev)
+    B = torch.ones((4, 10), dtype=torch.float32, device=dev)
+    fg.sgemm(A, B, f[:0], 1.0, 1.0)
+    fg.sgemm(torch.ones((10, 4), device=dev), torch.ones((4, 0), device=dev), f[:, :0], 1.0, 1.0)
+    torch.cuda.synchronize()
+    assert torch.all(big == CANARY).item()
+
+
+def test_alpha_zero_and_beta_zero(fg, dev, orc):
+    M, N, K = 300, 200, 100
+    A, B, C = inputs.make_random(M, N, K, seed=4)
+    cv = run(fg, dev, A, B, C, 0.0, 3.0)
+    assert np.array_equal(cv.result(), (3.0 * C.astype(np.float64)).astype(np.float32))
+    # beta == 0: the old C must not matter (finite "dirty" C).
+    _, r64 = orc.sgemm(A, B, np.zeros_like(C), 1.0, 0.0)
+    cv = run(fg, dev, A, B, C, 1.0, 0.0)
+    check_close(cv.result(), r64, K, A, B, "beta=0 dirty C")
+    cv0 = run(fg, dev, A, B, np.zeros_like(C), 1.0, 0.0)
+    assert np.array_equal(cv.result(), cv0.result())
+
+
+def test_alpha_beta_linearity(fg, dev, orc):
+    M, N, K = 384, 320, 256
+    A, B, C = inputs.make_random(M, N, K, seed=8)
+    P = run(fg, dev, A, B, np.zeros_like(C), 1.0, 0.0).result().astype(np.float64)
+    for alpha, beta in [(0.5, 3.0), (-2.0, 0.25)]:
+        got = run(fg, dev, A, B, C, alpha, beta).result().astype(np.float64)
+        want = alpha * P + beta * C.astype(np.float64)
+        assert np.max(np.abs(got - want)) / (K * np.abs(A).max() * np.abs(B).max()) <= 2 * TOL
+
+
+@pytest.mark.parametrize("pad", [3, 64])
+def test_padded_leading_dimensions(fg, dev, orc, pad):
+    M, N, K = 515, 260, 300
+    A, B, C = inputs.make_random(M, N, K, seed=pad)
+    _, r64 = orc.sgemm(A, B, C, 0.5, 3.0)
+    Abig = torch.full((M, K + pad), float("nan"), device=dev)
+    Bbig = torch.full((K, N + pad), float("nan"), device=dev)
+    Abig[:, :K] = torch.from_numpy(A).to(dev)
+    Bbig[:, :N] = torch.from_numpy(B).to(dev)
+    cv = Canvas(C, N + pad, 2, dev)
+    fg.sgemm(Abig[:, :K], Bbig[:, :N], cv.view, 0.5, 3.0)
+    torch.cuda.synchronize()
+    assert cv.untouched()
+    check_close(cv.result(), r64, K, A, B, f"pad {pad}")
+
+
+def test_misaligned_pointers_use_scalar_variant(fg, dev, orc):
+    M, N, K = 200, 256, 128
+    A, B, C = inputs.make_random(M, N, K, seed=9)
+    _, r64 = orc.sgemm(A, B, C, 1.0, 1.0)
+    Abuf = torch.zeros(M * K + 1, device=dev)
+    Abuf[1:] = torch.from_numpy(A.ravel()).to(dev)
+    Aoff = Abuf[1:].view(M, K)
+    assert Aoff.data_ptr() % 16 != 0
+    cv = Canvas(C, N, 1, dev)
+    fg.sgemm(Aoff, to_dev(B, dev), cv.view, 1.0, 1.0)
+    torch.cuda.synchronize()
+    check_close(cv.result(), r64, K, A, B, "misaligned A")
+
+
+def test_transpose_identity_bit_exact(fg, dev):
+    M, N, K = 8192 // 4, 2048 // 2, 777
+    A, B, C = inputs.make_small_int(M, N, K, seed=10)
+    Z = np.zeros((M, N), np.float32)
+    c1 = run(fg, dev, A, B, Z, 1.0, 0.0).result()
+    c2 = run(fg, dev, np.ascontiguousarray(B.T), np.ascontiguousarray(A.T), Z.T.copy(), 1.0, 0.0).result()
+    assert np.array_equal(c1.view(np.uint32), np.ascontiguousarray(c2.T).view(np.uint32))
+
+
+def test_overlap_rejected(fg, dev):
+    X = torch.zeros((256, 256), device=dev)
+    with pytest.raises(fg.SgemmError) as e:
+        fg.sgemm(X, X, X, 1.0, 0.0)
+    assert e.value.status == 3
+
+
+def test_side_stream(fg, dev, orc):
+    M, N, K = 512, 512, 512
+    A, B, C = inputs.make_random(M, N, K, seed=11)
+    _, r64 = orc.sgemm(A, B, C, 0.5, 3.0)
+    s = torch.cuda.Stream()
+    Ad, Bd, Cd = to_dev(A, dev), to_dev(B, dev), to_dev(C, dev)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        fg.sgemm_ex(Ad, Bd, Cd, 0.5, 3.0, stream=s)
+    s.synchronize()
+    check_close(Cd.cpu().numpy(), r64, K, A, B, "side stream")
