@@ -29,6 +29,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="sq4096")
     ap.add_argument("--cfg", type=int, default=-1, help="force a configuration id")
+    ap.add_argument("--tile", default=None,
+                    help="force the configuration with this comma-separated tuple")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
@@ -90,6 +92,12 @@ def main():
     torch.cuda.set_device(dev)
     if fg.device_check() != 0:
         raise SystemExit("bench.py: current device is not gfx950")
+    if args.tile:
+        want = tuple(int(x) for x in args.tile.split(","))
+        ids = [c["id"] for c in fg.configs() if c["tuple"][:len(want)] == want]
+        if not ids:
+            raise SystemExit(f"bench.py: no compiled configuration {want}")
+        args.cfg = ids[0]
     w = inputs.WORKLOADS[args.workload]
     A, B, C = inputs.make(w)
     Ad = torch.from_numpy(A).to(dev)

@@ -33,7 +33,7 @@ _i64, _i32, _f32, _vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c
 
 class _Config(ctypes.Structure):
     _fields_ = [(n, _i32) for n in (
-        "id", "path", "BM", "BN", "BK", "WM", "WN", "WNITER", "TM", "TN", "NT", "swz",
+        "id", "path", "BM", "BN", "BK", "WM", "WN", "WNITER", "TM", "TN", "NT", "swz", "opt",
         "WMITER", "WSUBM", "WSUBN", "acc_per_lane", "lds_bytes", "vgpr_estimate")]
 
 
@@ -64,6 +64,8 @@ _SIGS = {
     "sgemm_device_check": ([], ctypes.c_int),
     "sgemm_kernel_attributes": ([_i32, _i32, ctypes.POINTER(_Attr)], ctypes.c_int),
     "sgemm_check_tuple": ([ctypes.POINTER(_i32), _i32], ctypes.c_int),
+    "sgemm_tile_order": ([_i64, _i64, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32), _i64],
+                         _i64),
     "sgemm_simulate_tuple": ([ctypes.POINTER(_i32), _i32, ctypes.POINTER(_SimReport)],
                              ctypes.c_int),
 }
@@ -73,7 +75,7 @@ for _name, (_args, _res) in _SIGS.items():
     _fn.restype = _res
 
 PATHS = {0: "valu", 1: "mfma32", 2: "mfma16"}
-TUPLE_FIELDS = ("BM", "BN", "BK", "WM", "WN", "WNITER", "TM", "TN", "NT", "path", "swz")
+TUPLE_FIELDS = ("BM", "BN", "BK", "WM", "WN", "WNITER", "TM", "TN", "NT", "path", "swz", "opt")
 
 
 class SgemmError(RuntimeError):
@@ -124,12 +126,12 @@ def _kernel_resources():
     with open(_RESOURCES) as f:
         raw = json.load(f)
     out = {}
-    pat = re.compile(r"TileCfgILi" + r"ELi".join([r"(\d+)"] * 11) + r"EEELb(\d)")
+    pat = re.compile(r"TileCfgILi" + r"ELi".join([r"(\d+)"] * 12) + r"EEELb(\d)")
     for name, v in raw.items():
         m = pat.search(name)
         if m:
             g = tuple(int(x) for x in m.groups())
-            out[(g[:11], g[11])] = v
+            out[(g[:12], g[12])] = v
     return out
 
 
@@ -153,18 +155,34 @@ def kernel_attributes(cfg_id: int, vector_variant: bool = True) -> dict:
     return {f: getattr(a, f) for f, _ in _Attr._fields_}
 
 
+def _tuple12(tup):
+    tup = tuple(tup)
+    return (_i32 * 12)(*(tup + (0,) * (12 - len(tup))))
+
+
 def check_tuple(tup, target: str = "gfx950") -> int:
-    arr = (_i32 * 11)(*tup)
+    """Checker reason code; an 11-element tuple means opt = 0."""
+    arr = _tuple12(tup)
     return _lib.sgemm_check_tuple(arr, {"gfx950": 0, "page": 1}[target])
 
 
 def simulate_tuple(tup, banks: int = 32) -> dict:
-    arr = (_i32 * 11)(*tup)
+    arr = _tuple12(tup)
     r = _SimReport()
     rc = _lib.sgemm_simulate_tuple(arr, banks, ctypes.byref(r))
     d = {f: getattr(r, f) for f, _ in _SimReport._fields_}
     d["status"] = rc
     return d
+
+
+def tile_order(M, N, cfg_id):
+    """(rows, cols) output tile of each workgroup id, as lists."""
+    n = _lib.sgemm_tile_order(M, N, cfg_id, None, None, 0)
+    if n < 0:
+        raise ValueError("bad arguments")
+    r, c = (_i32 * n)(), (_i32 * n)()
+    _lib.sgemm_tile_order(M, N, cfg_id, r, c, n)
+    return list(r), list(c)
 
 
 def sgemm_raw(M, N, K, alpha, A_ptr, lda, B_ptr, ldb, beta, C_ptr, ldc, stream=None, cfg_id=-1):

@@ -38,7 +38,7 @@ VALU, MFMA32, MFMA16 = 0, 1, 2
 
 
 def candidates():
-    """Candidate tuples (BM, BN, BK, WM, WN, WNITER, TM, TN, NT, path, swz)."""
+    """Candidate tuples (BM, BN, BK, WM, WN, WNITER, TM, TN, NT, path, swz, opt)."""
     out = []
     # MFMA 32x32x2: every block/warp tile split into 1, 2, 4 or 8 waves.
     for BM, BN in [(256, 256), (256, 128), (128, 256), (128, 128), (128, 64), (64, 128), (64, 64)]:
@@ -50,13 +50,18 @@ def candidates():
                     waves = (BM // WM) * (BN // WN)
                     if waves not in (1, 2, 4, 8):
                         continue
-                    out.append((BM, BN, BK, WM, WN, WN // 32, 16, 1, 64 * waves, MFMA32, 32))
+                    base = (BM, BN, BK, WM, WN, WN // 32, 16, 1, 64 * waves, MFMA32, 32)
+                    out.append(base + (0,))
+                    # Schedule options on the larger tiles.
+                    if BM * BN >= 128 * 128 and BK >= 16:
+                        out += [base + (1,), base + (2,), base + (3,)]
     # MFMA 16x16x4: a few block shapes.
     for BM, BN, WM, WN in [(128, 128, 64, 64), (256, 128, 128, 64), (256, 256, 128, 128),
                            (64, 64, 32, 32), (128, 64, 64, 32)]:
         for BK in (16, 32):
             waves = (BM // WM) * (BN // WN)
-            out.append((BM, BN, BK, WM, WN, WN // 16, 4, 1, 64 * waves, MFMA16, 32))
+            base = (BM, BN, BK, WM, WN, WN // 16, 4, 1, 64 * waves, MFMA16, 32)
+            out += [base + (0,), base + (3,)]
     # VALU outer products: wave64 analogues of the page's shapes.
     for t in [
         (128, 128, 8, 64, 64, 1, 8, 8, 256),    # the page's square 128x128 tile, 8x8 lanes
@@ -69,14 +74,18 @@ def candidates():
         (256, 128, 16, 128, 64, 2, 8, 4, 256),
         (128, 128, 32, 64, 64, 2, 4, 4, 256),
     ]:
-        out.append(t + (VALU, 32))
+        out.append(t + (VALU, 32, 0))
+        out.append(t + (VALU, 32, 2))
     # Bank-model variants of the headline shapes: unswizzled, and 64 banks.
     for base in [(256, 256, 16, 128, 128, 4, 16, 1, 256, MFMA32),
+                 (256, 256, 32, 128, 128, 4, 16, 1, 256, MFMA32),
                  (128, 128, 16, 64, 64, 2, 16, 1, 256, MFMA32),
                  (128, 128, 16, 64, 64, 4, 4, 1, 256, MFMA16),
                  (128, 64, 16, 64, 64, 2, 4, 4, 128, VALU)]:
-        out.append(base + (0,))
-        out.append(base + (64,))
+        for swz in (0, 64):
+            out.append(base + (swz, 0))
+            if base[9] != VALU:
+                out.append(base + (swz, 3))
     seen, uniq = set(), []
     for t in out:
         if t not in seen:

@@ -41,7 +41,8 @@ struct KernelArgs {
   float* C;
   long long lda, ldb, ldc;
   int M, N, K;
-  int tiles_n;  // ceil(N / BN): the 1-D grid is tiles_m * tiles_n workgroups
+  int tiles_m, tiles_n;  // ceil(M / BM), ceil(N / BN): the 1-D grid has tiles_m * tiles_n workgroups
+  int group_m;           // tile rows per group of the XCD-aware order
   float alpha, beta;
 };
 
@@ -234,6 +235,80 @@ __device__ __forceinline__ void inner_product(const float* st, int wr0, int wc0,
   }
 }
 
+// ---- pipelined MFMA loop pieces ---------------------------------------------
+
+template <class Cfg>
+struct Frag {
+  float a[Cfg::WMITER];
+  float b[Cfg::WNITER];
+};
+
+// Fragments of the k-step starting at kk (one LDS read per sub-tile row/column).
+template <class Cfg>
+__device__ __forceinline__ void frag_load(const float* st, int kk, int wr0, int wc0, int lane,
+                                          Frag<Cfg>& f) {
+  constexpr Geom g = make_geom(Cfg::tile);
+  constexpr int blk = mfma_blk(g);
+  const int k = kk + mfma_frag_slot(g, lane), fr = mfma_frag_row(g, lane);
+#pragma unroll
+  for (int wm = 0; wm < g.WMITER; ++wm) f.a[wm] = st[as_index(g, k, wr0 + wm * blk + fr)];
+#pragma unroll
+  for (int wn = 0; wn < g.WNITER; ++wn) f.b[wn] = st[bs_index(g, k, wc0 + wn * blk + fr)];
+}
+
+template <class Cfg>
+__device__ __forceinline__ void mfma_step(const Frag<Cfg>& f, Acc<Cfg>& acc) {
+#pragma unroll
+  for (int wm = 0; wm < Cfg::WMITER; ++wm)
+#pragma unroll
+    for (int wn = 0; wn < Cfg::WNITER; ++wn) {
+      if constexpr (Cfg::PATH == kPathMfma32)
+        acc.v[wm][wn] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[wm], f.b[wn], acc.v[wm][wn], 0, 0, 0);
+      else
+        acc.v[wm][wn] = __builtin_amdgcn_mfma_f32_16x16x4f32(f.a[wm], f.b[wn], acc.v[wm][wn], 0, 0, 0);
+    }
+}
+
+// K loop with fragment double buffering.  Per slice kt (KS k-steps):
+//   issue the global loads of slice kt+1
+//   k-steps 0 .. KS-2: read fragments of step s+1, MFMAs of step s;
+//                      halfway, write slice kt+1 into the other LDS stage
+//   barrier
+//   read fragments of step 0 of slice kt+1, then MFMAs of step KS-1 of kt
+// The last iteration's extra loads are all masked (k0 >= K reads nothing)
+// and its extra LDS writes and reads touch only the unused stage, so the
+// loop body has no data-dependent branches.
+template <class Cfg, bool VEC>
+__device__ __forceinline__ void k_loop_pipelined(const KernelArgs& p, float* lds, int row0,
+                                                 int col0, int t, int wr0, int wc0, int lane,
+                                                 Acc<Cfg>& acc) {
+  constexpr Geom g = make_geom(Cfg::tile);
+  constexpr int kstep = mfma_kstep(g);
+  constexpr int KS = g.BK / kstep;
+  static_assert(KS % 2 == 0, "pipelined loop needs an even number of k-steps");
+  Staged<Cfg> s;
+  Frag<Cfg> f[2];
+  stage_load<Cfg, VEC>(p, row0, col0, 0, t, s);
+  stage_store<Cfg>(lds, t, s);
+  __syncthreads();
+  frag_load<Cfg>(lds, 0, wr0, wc0, lane, f[0]);
+  const int nk = (p.K + g.BK - 1) / g.BK;
+  for (int kt = 0; kt < nk; ++kt) {
+    const float* cur = lds + (kt & 1) * g.STAGE;
+    float* nxt = lds + ((kt + 1) & 1) * g.STAGE;
+    stage_load<Cfg, VEC>(p, row0, col0, (kt + 1) * g.BK, t, s);
+#pragma unroll
+    for (int st = 0; st < KS - 1; ++st) {
+      frag_load<Cfg>(cur, (st + 1) * kstep, wr0, wc0, lane, f[(st + 1) & 1]);
+      mfma_step<Cfg>(f[st & 1], acc);
+      if (st == KS / 2 - 1) stage_store<Cfg>(nxt, t, s);
+    }
+    __syncthreads();
+    frag_load<Cfg>(nxt, 0, wr0, wc0, lane, f[0]);
+    mfma_step<Cfg>(f[1], acc);
+  }
+}
+
 __device__ __forceinline__ void update_one(float* c, float acc, float alpha, float beta) {
   float v = alpha * acc;
   if (beta != 0.0f) v = __builtin_fmaf(beta, *c, v);
@@ -306,26 +381,31 @@ __global__ void __launch_bounds__(Cfg::NT) sgemm_tile_kernel(KernelArgs p) {
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int tile = blockIdx.x;
-  const int row0 = (tile / p.tiles_n) * g.BM;
-  const int col0 = (tile % p.tiles_n) * g.BN;
+  const TileRC tc = tile_of(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m,
+                            (Cfg::OPT & kOptXcdRemap) != 0);
+  const int row0 = tc.r * g.BM;
+  const int col0 = tc.c * g.BN;
   const int wr0 = wave_row0(g, wave), wc0 = wave_col0(g, wave);
 
   Acc<Cfg> acc;
   acc_zero(acc);
-  Staged<Cfg> s;
 
-  const int nk = (p.K + g.BK - 1) / g.BK;
-  stage_load<Cfg, VEC>(p, row0, col0, 0, t, s);
-  stage_store<Cfg>(lds, t, s);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const float* cur = lds + (kt & 1) * g.STAGE;
-    const bool more = kt + 1 < nk;
-    if (more) stage_load<Cfg, VEC>(p, row0, col0, (kt + 1) * g.BK, t, s);
-    inner_product<Cfg>(cur, wr0, wc0, lane, acc);
-    if (more) stage_store<Cfg>(lds + ((kt + 1) & 1) * g.STAGE, t, s);
+  if constexpr ((Cfg::OPT & kOptPipelined) != 0) {
+    k_loop_pipelined<Cfg, VEC>(p, lds, row0, col0, t, wr0, wc0, lane, acc);
+  } else {
+    Staged<Cfg> s;
+    const int nk = (p.K + g.BK - 1) / g.BK;
+    stage_load<Cfg, VEC>(p, row0, col0, 0, t, s);
+    stage_store<Cfg>(lds, t, s);
     __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const float* cur = lds + (kt & 1) * g.STAGE;
+      const bool more = kt + 1 < nk;
+      if (more) stage_load<Cfg, VEC>(p, row0, col0, (kt + 1) * g.BK, t, s);
+      inner_product<Cfg>(cur, wr0, wc0, lane, acc);
+      if (more) stage_store<Cfg>(lds + ((kt + 1) & 1) * g.STAGE, t, s);
+      __syncthreads();
+    }
   }
 
   const int rlim = min(g.WM, p.M - row0 - wr0);
@@ -336,12 +416,25 @@ __global__ void __launch_bounds__(Cfg::NT) sgemm_tile_kernel(KernelArgs p) {
 }
 
 // Host-side launcher for one instantiated tuple and variant.
+// Tile rows per group of the XCD-aware order: each XCD's share of the tiles
+// is made roughly square in elements (rows*BM ~ cols*BN), rounded down to a
+// power of two and clamped to the grid.
+inline int xcd_group_rows(long long tiles_m, long long tiles_n, int BM, int BN) {
+  const double per_xcd = static_cast<double>(tiles_m * tiles_n) / 8.0;
+  const double want = per_xcd * BN / BM;
+  int g = 1;
+  while (static_cast<double>(2 * g) * (2 * g) <= want && 2 * g <= tiles_m) g *= 2;
+  return g;
+}
+
 template <class Cfg, bool VEC>
 hipError_t launch_tile(const KernelArgs& a, hipStream_t stream) {
   KernelArgs k = a;
   const long long tiles_m = (a.M + Cfg::BM - 1) / Cfg::BM;
   const long long tiles_n = (a.N + Cfg::BN - 1) / Cfg::BN;
+  k.tiles_m = static_cast<int>(tiles_m);
   k.tiles_n = static_cast<int>(tiles_n);
+  k.group_m = xcd_group_rows(tiles_m, tiles_n, Cfg::BM, Cfg::BN);
   void* args[] = {&k};
   return hipLaunchKernel(reinterpret_cast<const void*>(&sgemm_tile_kernel<Cfg, VEC>),
                          dim3(static_cast<unsigned>(tiles_m * tiles_n)), dim3(Cfg::NT), args, 0,

@@ -36,6 +36,20 @@ enum Path : int { kPathValu = 0, kPathMfma32 = 1, kPathMfma16 = 2 };
 struct Tile {
   int BM, BN, BK, WM, WN, WNITER, TM, TN, NT, path;
   int swz;  // LDS bank count the As/Bs XOR swizzle is built for: 0 (none), 32 or 64
+  int opt;  // schedule options, a bit set of kOpt* below
+};
+
+// Schedule options.
+enum Opt : int {
+  // MFMA paths: fragment registers double-buffered across k-steps, the next
+  // slice's LDS stores placed mid-slice between MFMAs, and the next slice's
+  // first fragments read right after the barrier, ahead of the current
+  // slice's last k-step.
+  kOptPipelined = 1,
+  // Workgroup ids remapped so each XCD (the hardware hands consecutive ids to
+  // the 8 XCDs in turn) works on one compact block of output tiles.
+  kOptXcdRemap = 2,
+  kOptAll = 3,
 };
 
 // Machine limits the checker enforces.
@@ -79,7 +93,8 @@ enum Reason : int {
   kSwizzleRange = 16,       // swizzle needs BM, BN multiples of swz, BK <= swz, BK/4 a power of 2
   kRegisterEstimate = 17,   // estimated registers over the per-lane budget
   kNoMfmaOnTarget = 18,
-  kNumReasons = 19,
+  kBadOptions = 19,         // unknown option bits, or pipelining without an even k-step count
+  kNumReasons = 20,
 };
 
 constexpr int wmiter_of(const Tile& t, int wave) {
@@ -128,6 +143,7 @@ constexpr int check_tile(const Tile& t, const Target& m) {
       t.TM <= 0 || t.TN <= 0 || t.NT <= 0 || t.NT > 1024)
     return kBadRange;
   if (t.path != kPathValu && !m.allow_mfma) return kNoMfmaOnTarget;
+  if ((t.opt & ~kOptAll) != 0) return kBadOptions;
 
   // Whole waves, tiled evenly by warp tiles.
   if (t.NT % m.wave != 0) return kThreadsNotWaves;
@@ -172,6 +188,11 @@ constexpr int check_tile(const Tile& t, const Target& m) {
     const int kstep = (t.path == kPathMfma32) ? 2 : 4;
     if (wsubm != blk || wsubn != blk || t.TM != tm || t.TN != 1 || t.BK % kstep != 0)
       return kMfmaShape;
+    // The pipelined loop alternates two fragment buffers per k-step and
+    // relies on an even number of k-steps per slice.
+    if ((t.opt & kOptPipelined) && (t.BK / kstep) % 2 != 0) return kBadOptions;
+  } else if (t.opt & kOptPipelined) {
+    return kBadOptions;
   }
 
   if (m.gfx950_rules) {
@@ -204,9 +225,10 @@ constexpr bool tile_legal(const Tile& t) { return check_tile(t, kGfx950) == kLeg
 
 // Compile-time view of a legal tuple with its derived constants.
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int WNITER_, int TM_, int TN_, int NT_,
-          int PATH_, int SWZ_>
+          int PATH_, int SWZ_, int OPT_>
 struct TileCfg {
-  static constexpr Tile tile{BM_, BN_, BK_, WM_, WN_, WNITER_, TM_, TN_, NT_, PATH_, SWZ_};
+  static constexpr Tile tile{BM_, BN_, BK_, WM_, WN_, WNITER_, TM_, TN_, NT_, PATH_, SWZ_, OPT_};
+  static constexpr int OPT = OPT_;
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, WNITER = WNITER_;
   static constexpr int TM = TM_, TN = TN_, NT = NT_, PATH = PATH_;
   static constexpr int WAVE = 64;

@@ -43,7 +43,7 @@
 namespace fp32gemm {
 
 struct Geom {
-  int BM, BN, BK, WM, WN, WNITER, TM, TN, NT, path, swz;
+  int BM, BN, BK, WM, WN, WNITER, TM, TN, NT, path, swz, opt;
   int wave, WMITER, WSUBM, WSUBN, WAVES_N, KQ, NQ, ROWS_A, PASSES_A, ROWS_B, PASSES_B;
   int SA, SB, STAGE, ACC;
 };
@@ -51,7 +51,7 @@ struct Geom {
 constexpr Geom make_geom(const Tile& t) {
   Geom g{};
   g.BM = t.BM; g.BN = t.BN; g.BK = t.BK; g.WM = t.WM; g.WN = t.WN; g.WNITER = t.WNITER;
-  g.TM = t.TM; g.TN = t.TN; g.NT = t.NT; g.path = t.path; g.swz = t.swz;
+  g.TM = t.TM; g.TN = t.TN; g.NT = t.NT; g.path = t.path; g.swz = t.swz; g.opt = t.opt;
   g.wave = 64;
   g.WMITER = wmiter_of(t, 64);
   g.WSUBM = t.WM / g.WMITER;
@@ -133,6 +133,28 @@ FG_HD constexpr int mfma_out_row(const Geom& g, int l, int r) {
   return g.path == kPathMfma32 ? 8 * (r / 4) + 4 * (l / 32) + (r % 4) : 4 * (l / 16) + r;
 }
 FG_HD constexpr int mfma_out_col(const Geom& g, int l) { return l % mfma_blk(g); }
+
+// ---- workgroup -> output tile ----------------------------------------------
+// Plain order: tile row = id / tiles_n, tile column = id % tiles_n.
+// XCD-aware order: the hardware hands consecutive workgroup ids to the 8
+// XCDs in turn, so id -> (xcd = id % 8, local = id / 8) and each XCD gets one
+// contiguous run of a grouped raster (group_m tile rows per group, walked
+// column by column), i.e. a compact block of tiles sharing few A row panels
+// and B column panels in its L2.  Both orders are bijections onto the tiles.
+struct TileRC { int r, c; };
+FG_HD constexpr TileRC tile_of(int id, int tiles_m, int tiles_n, int group_m, bool xcd) {
+  if (!xcd) return TileRC{id / tiles_n, id % tiles_n};
+  const int ntiles = tiles_m * tiles_n;
+  const int q = ntiles / 8, rem = ntiles % 8;
+  const int x = id % 8, local = id / 8;
+  const int t = x * q + (x < rem ? x : rem) + local;
+  const int per_group = group_m * tiles_n;
+  const int grp = t / per_group;
+  const int first = grp * group_m;
+  const int gh = (tiles_m - first) < group_m ? (tiles_m - first) : group_m;
+  const int within = t - grp * per_group;
+  return TileRC{first + within % gh, within / gh};
+}
 
 // ---- output ownership (row, col within the block tile) ---------------------
 // Accumulator e of lane l in wave w.

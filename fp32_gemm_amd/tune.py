@@ -1,0 +1,191 @@
+"""Autotuner over the compiled tile tuples.
+
+For each shape and each compiled configuration whose kernels do not spill:
+launch once on integer-valued inputs and check sampled outputs exactly
+(every partial sum of small integers is exact in fp32, so a correct kernel
+matches int64 arithmetic bit for bit), then warm up and time on the
+workload's own inputs with HIP events.  The fastest few are re-timed with the
+longer protocol and the winner per shape goes into the dispatch table.  The
+page "Autotuning: Searching the Tile-Shape Space" (code listing and section
+"What The Sweep Found") describes the same launch / verify / time / record
+loop with a shorter warm-up for the sweep than for the final benchmark.
+
+    python -m fp32_gemm_amd.tune [--workloads a,b] [--out results.jsonl]
+                                 [--table-out tuned_table.inc]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+from . import binding as fg
+from . import inputs, model
+
+SHORT = (3, 10)   # warm-up, timed reps during the sweep
+LONG = (10, 50)   # re-timing of the finalists
+
+
+def _time(fn, warm, reps, stream):
+    for _ in range(warm):
+        fn()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(reps):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])
+    return float(np.median(per)), float(per.min()), float(per.max())
+
+
+def _exact_check(cfg_id, M, N, K, dev, samples=1500):
+    """Integer-valued inputs: sampled outputs must equal int64 arithmetic."""
+    A, B, C = inputs.make_small_int(M, N, K, seed=4242)
+    Ad, Bd = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+    Cd = torch.from_numpy(C).to(dev)
+    fg.sgemm_ex(Ad, Bd, Cd, 0.5, 3.0, cfg_id=cfg_id)
+    torch.cuda.synchronize()
+    rows, cols = inputs.sample_indices(M, N, samples, seed=4243)
+    got = Cd.cpu().numpy()[rows, cols]
+    s = np.einsum("ij,ji->i", A[rows].astype(np.int64), B[:, cols].astype(np.int64))
+    want = (0.5 * s + 3.0 * C[rows, cols].astype(np.float64)).astype(np.float32)
+    return bool(np.array_equal(got.view(np.uint32), want.view(np.uint32)))
+
+
+def usable_configs():
+    out = []
+    for c in fg.configs():
+        rv, rs = c["resources_vec"], c["resources_scalar"]
+        if rv is None or rs is None or rv.get("ScratchSize", 1) > 0:
+            continue
+        out.append(c)
+    return out
+
+
+def tune_shape(w, dev, configs, log, finalists=4):
+    A, B, C = inputs.make(w)
+    Ad, Bd = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+    Cd = torch.from_numpy(C).to(dev)
+    stream = torch.cuda.current_stream(dev)
+    flops = model.flops(w.M, w.N, w.K)
+    results = []
+    for c in configs:
+        ok = _exact_check(c["id"], w.M, w.N, w.K, dev)
+        rec = {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "cfg_id": c["id"],
+               "tuple": list(c["tuple"]), "path": c["path_name"], "exact": ok}
+        if ok:
+            med, lo, hi = _time(lambda: fg.sgemm_ex(Ad, Bd, Cd, w.alpha, w.beta, stream=stream,
+                                                    cfg_id=c["id"]), *SHORT, stream)
+            rec.update(ms=med, ms_min=lo, ms_max=hi, tflops=flops / (med * 1e-3) / 1e12,
+                       protocol="short")
+        results.append(rec)
+        log(rec)
+    ok = sorted((r for r in results if r["exact"]), key=lambda r: r["ms"])
+    for r in ok[:finalists]:
+        med, lo, hi = _time(lambda: fg.sgemm_ex(Ad, Bd, Cd, w.alpha, w.beta, stream=stream,
+                                                cfg_id=r["cfg_id"]), *LONG, stream)
+        fin = dict(r, ms=med, ms_min=lo, ms_max=hi, tflops=flops / (med * 1e-3) / 1e12,
+                   protocol="long")
+        results.append(fin)
+        log(fin)
+    best = min((r for r in results if r.get("protocol") == "long"), key=lambda r: r["ms"])
+    return best, results
+
+
+def write_table(best_by_shape, path, defaults):
+    lines = [
+        "// tuned_table.inc -- dispatch table for the tuned choice of tile tuple.",
+        "//",
+        "// kTuned lists shapes with the tuple the autotuner measured fastest on",
+        "// them (fp32_gemm_amd/tune.py); other shapes take the tuned rule nearest in",
+        "// log(M), log(N), log(K).  Tuple order:",
+        "// {BM, BN, BK, WM, WN, WNITER, TM, TN, NT, path, swz}.",
+        "",
+        "static const TunedRule kTuned[] = {",
+    ]
+    for b in best_by_shape:
+        t = b["tuple"]
+        lines.append("    {%d, %d, %d, {%s}},  // %s: %.3f ms, %.1f TFLOP/s" % (
+            b["M"], b["N"], b["K"], ", ".join(str(x) for x in t), b["workload"], b["ms"],
+            b["tflops"]))
+    lines.append("};")
+    lines.append("")
+    for name, t in defaults:
+        lines.append("static constexpr Tile %s{%s};" % (name, ", ".join(str(x) for x in t)))
+    lines.append("")
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workloads", default=",".join(inputs.WORKLOADS))
+    ap.add_argument("--out", default="gpurun_out/tune_results.jsonl")
+    ap.add_argument("--table-out", default=None)
+    ap.add_argument("--paths", default="valu,mfma32,mfma16")
+    ap.add_argument("--prune-above", type=float, default=2 * 4096 ** 3 * 1.5,
+                    help="shapes with more FLOP than this only try the best --keep configs "
+                         "of the largest shape already swept")
+    ap.add_argument("--keep", type=int, default=32)
+    ap.add_argument("--best", default=None,
+                    help="print the best tuple recorded for this workload in --out and exit")
+    args = ap.parse_args()
+    if args.best:
+        recs = [json.loads(l) for l in open(args.out)]
+        fin = [r for r in recs if r["workload"] == args.best and r.get("protocol") == "long"]
+        print(",".join(str(x) for x in min(fin, key=lambda r: r["ms"])["tuple"]))
+        return 0
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if fg.device_check() != 0:
+        raise SystemExit("tune: current device is not gfx950")
+    paths = set(args.paths.split(","))
+    configs = [c for c in usable_configs() if c["path_name"] in paths]
+    os.makedirs(os.path.dirname(args.out) or ".", exist_ok=True)
+    fout = open(args.out, "a")
+
+    def log(rec):
+        fout.write(json.dumps(rec) + "\n")
+        fout.flush()
+        if rec.get("protocol") == "long" or not rec["exact"]:
+            print(json.dumps(rec), flush=True)
+
+    bests = []
+    ranked = None  # configs of the largest shape swept so far, fastest first
+    names = sorted(args.workloads.split(","), key=lambda n: model.flops(
+        inputs.WORKLOADS[n].M, inputs.WORKLOADS[n].N, inputs.WORKLOADS[n].K))
+    for name in names:
+        w = inputs.WORKLOADS[name]
+        t0 = time.time()
+        use = configs
+        if ranked is not None and model.flops(w.M, w.N, w.K) > args.prune_above:
+            use = ranked[:args.keep]
+        print(f"[tune] {name}: {len(use)} configs", flush=True)
+        best, results = tune_shape(w, dev, use, log)
+        if model.flops(w.M, w.N, w.K) <= args.prune_above:
+            order = sorted((r for r in results if r.get("protocol") == "short" and r["exact"]),
+                           key=lambda r: r["ms"])
+            by_id = {c["id"]: c for c in configs}
+            ranked = [by_id[r["cfg_id"]] for r in order]
+        print(f"[tune] {name}: best cfg {best['cfg_id']} {best['tuple']} {best['ms']:.4f} ms "
+              f"{best['tflops']:.1f} TFLOP/s ({time.time() - t0:.0f} s)", flush=True)
+        bests.append(best)
+    if args.table_out:
+        by = {b["workload"]: b["tuple"] for b in bests}
+        large = by.get("sq4096", bests[0]["tuple"])
+        medium = by.get("sq1024", large)
+        small = by.get("sq256", medium)
+        write_table(bests, args.table_out, [("kDefaultLarge", large), ("kDefaultMedium", medium),
+                                            ("kDefaultSmall", small)])
+    fout.close()
+
+
+if __name__ == "__main__":
+    sys.exit(main())

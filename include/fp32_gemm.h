@@ -92,6 +92,7 @@ typedef struct sgemm_config_t {
   int32_t path;
   int32_t BM, BN, BK, WM, WN, WNITER, TM, TN, NT;
   int32_t swz; /* 0 = unswizzled LDS, 32 or 64 = XOR swizzle for that bank count */
+  int32_t opt; /* schedule options: bit 0 pipelined MFMA loop, bit 1 XCD-aware tile order */
   int32_t WMITER, WSUBM, WSUBN;
   int32_t acc_per_lane;
   int32_t lds_bytes;     /* both LDS stages */
@@ -135,16 +136,24 @@ typedef struct sgemm_kernel_attr_t {
 } sgemm_kernel_attr_t;
 int sgemm_kernel_attributes(int32_t id, int32_t vector_variant, sgemm_kernel_attr_t* out);
 
+/* Output tile (row, column in tiles) of each workgroup id for this shape and
+ * configuration: fills rows[id], cols[id] for id < min(count, capacity) and
+ * returns count = ceil(M/BM) * ceil(N/BN), or -1 for bad arguments.  With
+ * the XCD-aware option the order groups each XCD's workgroups into one block
+ * of tiles; it is a bijection either way. */
+int64_t sgemm_tile_order(int64_t M, int64_t N, int32_t cfg_id, int32_t* rows, int32_t* cols,
+                         int64_t capacity);
+
 /* ---- legality checker and index-map simulator ------------------------------ */
 
-/* tuple = {BM, BN, BK, WM, WN, WNITER, TM, TN, NT, path, swz}.
+/* tuple = {BM, BN, BK, WM, WN, WNITER, TM, TN, NT, path, swz, opt}.
  * target 0 = gfx950 (wave64, 160 KiB LDS, double buffering, register
  * budget); target 1 = the page's own machine model (32-lane warps, 48 KB
  * shared memory, single buffer, <= 128 accumulators), as used by "Autotuning:
  * Searching the Tile-Shape Space".  Returns 0 if legal, else the positive
  * reason code of the first failing guard (see tile_config.hpp), or -1 for a
  * bad target. */
-int sgemm_check_tuple(const int32_t tuple[11], int32_t target);
+int sgemm_check_tuple(const int32_t tuple[12], int32_t target);
 
 /* Runs the kernels' own index maps on the host for a gfx950-legal tuple and
  * checks: every C element of the block tile owned by exactly one
@@ -162,7 +171,7 @@ typedef struct sgemm_sim_report_t {
   int32_t read_a_ways;    /* fragment reads of As */
   int32_t read_b_ways;    /* fragment reads of Bs */
 } sgemm_sim_report_t;
-int sgemm_simulate_tuple(const int32_t tuple[11], int32_t banks, sgemm_sim_report_t* out);
+int sgemm_simulate_tuple(const int32_t tuple[12], int32_t banks, sgemm_sim_report_t* out);
 
 #ifdef __cplusplus
 }

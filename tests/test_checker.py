@@ -157,3 +157,33 @@ def test_traffic_model_matches_page_numbers():
 def test_peak_numbers():
     assert abs(model.PEAK_FP32_TFLOPS - 157.286) < 0.01
     assert abs(model.PEAK_FP32_VALU_UNPACKED_TFLOPS - 78.643) < 0.01
+
+
+def test_option_guard():
+    # Pipelining is an MFMA-loop option and needs an even number of k-steps.
+    assert fg.check_tuple((128, 64, 16, 64, 64, 2, 4, 4, 128, VALU, 32, 1)) == 19
+    assert fg.check_tuple((128, 128, 4, 128, 64, 4, 4, 1, 128, MFMA16, 0, 1)) == 19
+    assert fg.check_tuple((128, 128, 16, 64, 64, 2, 16, 1, 256, MFMA32, 32, 8)) == 19
+    assert fg.check_tuple((128, 128, 16, 64, 64, 2, 16, 1, 256, MFMA32, 32, 3)) == 0
+
+
+@pytest.mark.parametrize("M,N", [(4096, 4096), (4097, 4095), (8192, 2048), (1000, 1500), (256, 256),
+                                 (300, 7000), (65, 64), (8192, 8192)])
+def test_tile_order_is_a_bijection(M, N):
+    for c in fg.configs():
+        if c["opt"] & 2 == 0 and (M, N) != (4096, 4096):
+            continue
+        rows, cols = fg.tile_order(M, N, c["id"])
+        tm, tn = -(-M // c["BM"]), -(-N // c["BN"])
+        assert len(rows) == tm * tn
+        assert sorted(zip(rows, cols)) == [(r, q) for r in range(tm) for q in range(tn)]
+
+
+def test_xcd_order_gives_each_xcd_a_compact_block():
+    c = [x for x in fg.configs() if x["tuple"][:11] == (256, 256, 16, 128, 128, 4, 16, 1, 256, 1, 32)
+         and x["opt"] & 2][0]
+    rows, cols = fg.tile_order(4096, 4096, c["id"])
+    for x in range(8):
+        mine = [(rows[i], cols[i]) for i in range(len(rows)) if i % 8 == x]
+        # 32 tiles of a 16 x 16 grid in a 4 x 8 block: 4 A row panels, 8 B column panels.
+        assert len({r for r, _ in mine}) == 4 and len({q for _, q in mine}) == 8
