@@ -106,7 +106,7 @@ def write_table(best_by_shape, path, defaults):
         "// kTuned lists shapes with the tuple the autotuner measured fastest on",
         "// them (fp32_gemm_amd/tune.py); other shapes take the tuned rule nearest in",
         "// log(M), log(N), log(K).  Tuple order:",
-        "// {BM, BN, BK, WM, WN, WNITER, TM, TN, NT, path, swz}.",
+        "// {BM, BN, BK, WM, WN, WNITER, TM, TN, NT, path, swz, opt}.",
         "",
         "static const TunedRule kTuned[] = {",
     ]
