@@ -179,26 +179,34 @@ __device__ __forceinline__ void inner_product(const float* st, int wr0, int wc0,
   constexpr Geom g = make_geom(Cfg::tile);
   if constexpr (Cfg::PATH == kPathValu) {
     // Outer product of regM (WMITER*TM values down m) and regN (WNITER*TN
-    // values along n) per k, the page's third tiling level; 128-bit LDS reads.
-#pragma unroll
-    for (int k = 0; k < g.BK; ++k) {
-      float rm[g.WMITER * g.TM], rn[g.WNITER * g.TN];
+    // values along n) per k, the page's third tiling level, with 128-bit LDS
+    // reads.  The fragments of k+1 are read while the FMAs of k run; the
+    // scheduling barrier per k-step keeps the compiler from hoisting every
+    // read of the slice (which would need BK sets of fragment registers).
+    float rm[2][g.WMITER * g.TM], rn[2][g.WNITER * g.TN];
+    auto load = [&](int k, int b) {
 #pragma unroll
       for (int wm = 0; wm < g.WMITER; ++wm)
 #pragma unroll
         for (int i = 0; i < g.TM; i += 4) {
           const f32x4 v = *reinterpret_cast<const f32x4*>(&st[as_index(g, k, wr0 + valu_m(g, lane, wm, i))]);
-          rm[wm * g.TM + i + 0] = v[0]; rm[wm * g.TM + i + 1] = v[1];
-          rm[wm * g.TM + i + 2] = v[2]; rm[wm * g.TM + i + 3] = v[3];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) rm[b][wm * g.TM + i + q] = v[q];
         }
 #pragma unroll
       for (int wn = 0; wn < g.WNITER; ++wn)
 #pragma unroll
         for (int j = 0; j < g.TN; j += 4) {
           const f32x4 v = *reinterpret_cast<const f32x4*>(&st[bs_index(g, k, wc0 + valu_n(g, lane, wn, j))]);
-          rn[wn * g.TN + j + 0] = v[0]; rn[wn * g.TN + j + 1] = v[1];
-          rn[wn * g.TN + j + 2] = v[2]; rn[wn * g.TN + j + 3] = v[3];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) rn[b][wn * g.TN + j + q] = v[q];
         }
+    };
+    load(0, 0);
+#pragma unroll
+    for (int k = 0; k < g.BK; ++k) {
+      if (k + 1 < g.BK) load(k + 1, (k + 1) & 1);
+      const int b = k & 1;
 #pragma unroll
       for (int wm = 0; wm < g.WMITER; ++wm)
 #pragma unroll
@@ -208,8 +216,9 @@ __device__ __forceinline__ void inner_product(const float* st, int wr0, int wc0,
 #pragma unroll
             for (int j = 0; j < g.TN; ++j) {
               float& a = acc.v[valu_acc_index(g, wm, i, wn, j)];
-              a = __builtin_fmaf(rm[wm * g.TM + i], rn[wn * g.TN + j], a);
+              a = __builtin_fmaf(rm[b][wm * g.TM + i], rn[b][wn * g.TN + j], a);
             }
+      __builtin_amdgcn_sched_barrier(0);
     }
   } else {
     constexpr int blk = mfma_blk(g), kstep = mfma_kstep(g);
