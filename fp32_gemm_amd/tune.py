@@ -134,6 +134,10 @@ def main():
                     help="shapes with more FLOP than this only try the best --keep configs "
                          "of the largest shape already swept")
     ap.add_argument("--keep", type=int, default=32)
+    ap.add_argument("--top-from", default=None,
+                    help="only try tuples ranked in the top --top of a previous results file "
+                         "(per workload, short protocol)")
+    ap.add_argument("--top", type=int, default=24)
     ap.add_argument("--best", default=None,
                     help="print the best tuple recorded for this workload in --out and exit")
     args = ap.parse_args()
@@ -148,6 +152,14 @@ def main():
         raise SystemExit("tune: current device is not gfx950")
     paths = set(args.paths.split(","))
     configs = [c for c in usable_configs() if c["path_name"] in paths]
+    if args.top_from:
+        prev = [json.loads(l) for l in open(args.top_from)]
+        keep = set()
+        for wl in {r["workload"] for r in prev}:
+            rs = sorted((r for r in prev if r["workload"] == wl and r.get("protocol") == "short"
+                         and r["exact"]), key=lambda r: r["ms"])
+            keep |= {tuple(r["tuple"]) for r in rs[:args.top]}
+        configs = [c for c in configs if tuple(c["tuple"]) in keep]
     os.makedirs(os.path.dirname(args.out) or ".", exist_ok=True)
     fout = open(args.out, "a")
 
