@@ -76,6 +76,12 @@ def candidates():
     ]:
         out.append(t + (VALU, 32, 0))
         out.append(t + (VALU, 32, 2))
+    # The same schedules with the global loads left to the compiler.
+    for base in [(256, 256, 32, 64, 128, 4, 16, 1, 512, MFMA32, 32),
+                 (256, 256, 32, 128, 64, 2, 16, 1, 512, MFMA32, 32),
+                 (128, 128, 32, 32, 64, 2, 16, 1, 512, MFMA32, 32),
+                 (256, 256, 16, 64, 128, 4, 16, 1, 512, MFMA32, 32)]:
+        out += [base + (4,), base + (7,)]
     # Bank-model variants of the headline shapes: unswizzled, and 64 banks.
     for base in [(256, 256, 16, 128, 128, 4, 16, 1, 256, MFMA32),
                  (256, 256, 32, 128, 128, 4, 16, 1, 256, MFMA32),

@@ -308,8 +308,9 @@ __device__ __forceinline__ void k_loop_pipelined(const KernelArgs& p, float* lds
     stage_load<Cfg, VEC>(p, row0, col0, (kt + 1) * g.BK, t, s);
     // Keep the global loads at the top of the slice: left to itself the
     // scheduler sinks them next to their LDS stores, exposing the full
-    // memory latency once per slice.
-    __builtin_amdgcn_sched_barrier(0);
+    // memory latency once per slice.  (The scalar variant's four times more
+    // load offsets would not fit the register budget that way.)
+    if constexpr (VEC && !(Cfg::OPT & kOptFloatLoads)) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int st = 0; st < KS - 1; ++st) {
       frag_load<Cfg>(cur, (st + 1) * kstep, wr0, wc0, lane, f[(st + 1) & 1]);
@@ -415,7 +416,7 @@ __global__ void __launch_bounds__(Cfg::NT) sgemm_tile_kernel(KernelArgs p) {
       const float* cur = lds + (kt & 1) * g.STAGE;
       const bool more = kt + 1 < nk;
       if (more) stage_load<Cfg, VEC>(p, row0, col0, (kt + 1) * g.BK, t, s);
-      __builtin_amdgcn_sched_barrier(0);  // loads stay ahead of the inner product
+      if constexpr (VEC && !(Cfg::OPT & kOptFloatLoads)) __builtin_amdgcn_sched_barrier(0);  // loads stay ahead of the inner product
       inner_product<Cfg>(cur, wr0, wc0, lane, acc);
       if (more) stage_store<Cfg>(lds + ((kt + 1) & 1) * g.STAGE, t, s);
       __syncthreads();

@@ -49,7 +49,11 @@ enum Opt : int {
   // Workgroup ids remapped so each XCD (the hardware hands consecutive ids to
   // the 8 XCDs in turn) works on one compact block of output tiles.
   kOptXcdRemap = 2,
-  kOptAll = 3,
+  // Let the compiler place each slice's global loads (by default they are
+  // pinned to the top of the slice in the float4 variant); kept so the two
+  // schedules can be compared in one process.
+  kOptFloatLoads = 4,
+  kOptAll = 7,
 };
 
 // Machine limits the checker enforces.

@@ -69,7 +69,7 @@ def usable_configs():
     return out
 
 
-def tune_shape(w, dev, configs, log, finalists=4):
+def tune_shape(w, dev, configs, log, finalists=6):
     A, B, C = inputs.make(w)
     Ad, Bd = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
     Cd = torch.from_numpy(C).to(dev)
@@ -87,12 +87,30 @@ def tune_shape(w, dev, configs, log, finalists=4):
                        protocol="short")
         results.append(rec)
         log(rec)
-    ok = sorted((r for r in results if r["exact"]), key=lambda r: r["ms"])
-    for r in ok[:finalists]:
-        med, lo, hi = _time(lambda: fg.sgemm_ex(Ad, Bd, Cd, w.alpha, w.beta, stream=stream,
-                                                cfg_id=r["cfg_id"]), *LONG, stream)
-        fin = dict(r, ms=med, ms_min=lo, ms_max=hi, tflops=flops / (med * 1e-3) / 1e12,
-                   protocol="long")
+    ok = sorted((r for r in results if r["exact"]), key=lambda r: r["ms"])[:finalists]
+    # Finalists are timed interleaved (one batch of each in turn, repeated),
+    # so clock and temperature drift affect them alike.
+    warm, reps = LONG
+    batch = 5
+    fns = [lambda r=r: fg.sgemm_ex(Ad, Bd, Cd, w.alpha, w.beta, stream=stream, cfg_id=r["cfg_id"])
+           for r in ok]
+    for f in fns:
+        for _ in range(warm):
+            f()
+    samples = [[] for _ in ok]
+    for _ in range(reps // batch):
+        for i, f in enumerate(fns):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(batch):
+                f()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            samples[i].append(e0.elapsed_time(e1) / batch)
+    for r, smp in zip(ok, samples):
+        med = float(np.median(smp))
+        fin = dict(r, ms=med, ms_min=float(min(smp)), ms_max=float(max(smp)),
+                   tflops=flops / (med * 1e-3) / 1e12, protocol="long")
         results.append(fin)
         log(fin)
     best = min((r for r in results if r.get("protocol") == "long"), key=lambda r: r["ms"])
@@ -138,6 +156,9 @@ def main():
                     help="only try tuples ranked in the top --top of a previous results file "
                          "(per workload, short protocol)")
     ap.add_argument("--top", type=int, default=24)
+    ap.add_argument("--filter", default=None,
+                    help="Python expression over a config dict c (e.g. \"c['BK'] == 32\")")
+    ap.add_argument("--finalists", type=int, default=6)
     ap.add_argument("--best", default=None,
                     help="print the best tuple recorded for this workload in --out and exit")
     args = ap.parse_args()
@@ -160,6 +181,8 @@ def main():
                          and r["exact"]), key=lambda r: r["ms"])
             keep |= {tuple(r["tuple"]) for r in rs[:args.top]}
         configs = [c for c in configs if tuple(c["tuple"]) in keep]
+    if args.filter:
+        configs = [c for c in configs if eval(args.filter, {}, {"c": c})]
     os.makedirs(os.path.dirname(args.out) or ".", exist_ok=True)
     fout = open(args.out, "a")
 
@@ -180,7 +203,7 @@ def main():
         if ranked is not None and model.flops(w.M, w.N, w.K) > args.prune_above:
             use = ranked[:args.keep]
         print(f"[tune] {name}: {len(use)} configs", flush=True)
-        best, results = tune_shape(w, dev, use, log)
+        best, results = tune_shape(w, dev, use, log, finalists=args.finalists)
         if model.flops(w.M, w.N, w.K) <= args.prune_above:
             order = sorted((r for r in results if r.get("protocol") == "short" and r["exact"]),
                            key=lambda r: r["ms"])

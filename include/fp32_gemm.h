@@ -92,7 +92,8 @@ typedef struct sgemm_config_t {
   int32_t path;
   int32_t BM, BN, BK, WM, WN, WNITER, TM, TN, NT;
   int32_t swz; /* 0 = unswizzled LDS, 32 or 64 = XOR swizzle for that bank count */
-  int32_t opt; /* schedule options: bit 0 pipelined MFMA loop, bit 1 XCD-aware tile order */
+  int32_t opt; /* schedule options: bit 0 pipelined MFMA loop, bit 1 XCD-aware tile order,
+                  bit 2 unpinned global loads */
   int32_t WMITER, WSUBM, WSUBN;
   int32_t acc_per_lane;
   int32_t lds_bytes;     /* both LDS stages */
