@@ -176,9 +176,9 @@ def main():
         "roofline": {
             "bound": "mfma" if info["path"] != 0 else "alu",
             "achieved": round(achieved, 2),
-            "peak": round(peak if info["path"] != 0 else model.PEAK_FP32_VALU_UNPACKED_TFLOPS, 1),
+            "peak": round(peak, 1),
             "unit": "TFLOP/s",
-            "frac": round(achieved / (peak if info["path"] != 0 else model.PEAK_FP32_VALU_UNPACKED_TFLOPS), 4),
+            "frac": round(achieved / peak, 4),
             "traffic": traffic,
         },
         "timing_ms": {"event_avg": round(avg_ms, 4), "median": round(float(np.median(per)), 4),

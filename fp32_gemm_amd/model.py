@@ -12,8 +12,9 @@ from __future__ import annotations
 CUS = 256
 CLOCK_HZ = 2.4e9
 FP32_FLOP_PER_CLK_PER_CU = 256          # MFMA fp32, or VALU with packed FMA
-PEAK_FP32_TFLOPS = CUS * CLOCK_HZ * FP32_FLOP_PER_CLK_PER_CU / 1e12   # 157.3
-# The VALU path issues one non-packed v_fma_f32 per lane per cycle: half the peak.
+PEAK_FP32_TFLOPS = CUS * CLOCK_HZ * FP32_FLOP_PER_CLK_PER_CU / 1e12   # 157.3 (matrix and vector)
+# Without packed-FP32 instructions a lane retires one FMA per cycle: half the
+# published vector peak (a register-only probe measures 75.8 TFLOP/s).
 PEAK_FP32_VALU_UNPACKED_TFLOPS = PEAK_FP32_TFLOPS / 2                  # 78.6
 PEAK_HBM_GBS = 8000.0
 
