@@ -38,7 +38,8 @@ class _Config(ctypes.Structure):
 
 
 class _Plan(ctypes.Structure):
-    _fields_ = [("cfg_id", _i32), ("vector_variant", _i32), ("grid", _i64), ("block", _i32)]
+    _fields_ = [("cfg_id", _i32), ("vector_variant", _i32), ("grid", _i64), ("block", _i32),
+                ("tiles_full", _i32), ("splits", _i32)]
 
 
 class _Attr(ctypes.Structure):

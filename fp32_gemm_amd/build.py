@@ -76,6 +76,18 @@ def candidates():
     ]:
         out.append(t + (VALU, 32, 0))
         out.append(t + (VALU, 32, 2))
+    # Split-K of a partly filled last wave, on the shapes ragged or small
+    # problems use.
+    for base in [(256, 256, 32, 64, 128, 4, 16, 1, 512, MFMA32, 32),
+                 (256, 256, 16, 64, 128, 4, 16, 1, 512, MFMA32, 32),
+                 (128, 128, 32, 32, 64, 2, 16, 1, 512, MFMA32, 32),
+                 (128, 128, 16, 32, 64, 2, 16, 1, 512, MFMA32, 32),
+                 (128, 128, 32, 64, 64, 2, 16, 1, 256, MFMA32, 32),
+                 (128, 256, 32, 64, 128, 4, 16, 1, 256, MFMA32, 32),
+                 (256, 128, 32, 128, 64, 2, 16, 1, 256, MFMA32, 32),
+                 (64, 64, 32, 32, 32, 1, 16, 1, 256, MFMA32, 32),
+                 (128, 128, 16, 64, 64, 4, 4, 1, 256, MFMA16, 32)]:
+        out += [base + (8,), base + (9,), base + (11,), base + (15,)]
     # The same schedules with the global loads left to the compiler.
     for base in [(256, 256, 32, 64, 128, 4, 16, 1, 512, MFMA32, 32),
                  (256, 256, 32, 128, 64, 2, 16, 1, 512, MFMA32, 32),

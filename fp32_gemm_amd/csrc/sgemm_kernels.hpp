@@ -41,8 +41,11 @@ struct KernelArgs {
   float* C;
   long long lda, ldb, ldc;
   int M, N, K;
-  int tiles_m, tiles_n;  // ceil(M / BM), ceil(N / BN): the 1-D grid has tiles_m * tiles_n workgroups
+  int tiles_m, tiles_n;  // ceil(M / BM), ceil(N / BN)
   int group_m;           // tile rows per group of the XCD-aware order
+  int nk;                // K slices per tile: ceil(K / BK)
+  int tiles_full;        // tiles computed whole, one workgroup each
+  int splits;            // K segments of each remaining tile (1 = no split)
   float alpha, beta;
 };
 
@@ -290,21 +293,20 @@ __device__ __forceinline__ void mfma_step(const Frag<Cfg>& f, Acc<Cfg>& acc) {
 template <class Cfg, bool VEC>
 __device__ __forceinline__ void k_loop_pipelined(const KernelArgs& p, float* lds, int row0,
                                                  int col0, int t, int wr0, int wc0, int lane,
-                                                 Acc<Cfg>& acc) {
+                                                 int kt0, int kt1, Acc<Cfg>& acc) {
   constexpr Geom g = make_geom(Cfg::tile);
   constexpr int kstep = mfma_kstep(g);
   constexpr int KS = g.BK / kstep;
   static_assert(KS % 2 == 0, "pipelined loop needs an even number of k-steps");
   Staged<Cfg> s;
   Frag<Cfg> f[2];
-  stage_load<Cfg, VEC>(p, row0, col0, 0, t, s);
+  stage_load<Cfg, VEC>(p, row0, col0, kt0 * g.BK, t, s);
   stage_store<Cfg>(lds, t, s);
   __syncthreads();
   frag_load<Cfg>(lds, 0, wr0, wc0, lane, f[0]);
-  const int nk = (p.K + g.BK - 1) / g.BK;
-  for (int kt = 0; kt < nk; ++kt) {
-    const float* cur = lds + (kt & 1) * g.STAGE;
-    float* nxt = lds + ((kt + 1) & 1) * g.STAGE;
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const float* cur = lds + ((kt - kt0) & 1) * g.STAGE;
+    float* nxt = lds + ((kt - kt0 + 1) & 1) * g.STAGE;
     stage_load<Cfg, VEC>(p, row0, col0, (kt + 1) * g.BK, t, s);
     // Keep the global loads at the top of the slice: left to itself the
     // scheduler sinks them next to their LDS stores, exposing the full
@@ -386,6 +388,41 @@ __device__ __forceinline__ void epilogue(float* cw, int ldc, int rlim, int clim,
   }
 }
 
+// Split segments: C += alpha * partial with fp32 atomics (C already holds
+// beta * C for these tiles).
+template <class Cfg>
+__device__ __forceinline__ void epilogue_atomic(float* cw, int ldc, int rlim, int clim, int lane,
+                                                float alpha, const Acc<Cfg>& acc) {
+  constexpr Geom g = make_geom(Cfg::tile);
+#pragma unroll
+  for (int e = 0; e < g.ACC; ++e) {
+    const RC rc = owner(g, 0, lane, e);  // position inside the wave tile (wave 0's origin is 0,0)
+    float v;
+    if constexpr (Cfg::PATH == kPathValu) {
+      v = acc.v[e];
+    } else {
+      constexpr int regs = mfma_regs(g);
+      v = acc.v[(e / regs) / g.WNITER][(e / regs) % g.WNITER][e % regs];
+    }
+    if (rc.r < rlim && rc.c < clim) unsafeAtomicAdd(cw + rc.r * ldc + rc.c, alpha * v);
+  }
+}
+
+// Pre-pass for split tiles: C <- beta * C on the tiles at tile-order positions
+// [p.tiles_full, tiles_m * tiles_n) (zero when beta == 0, without reading C).
+template <int BM, int BN, bool GROUPED>
+__global__ void __launch_bounds__(256) sgemm_scale_tiles_kernel(KernelArgs p) {
+  const TileRC tc = tile_at(p.tiles_full + static_cast<int>(blockIdx.x), p.tiles_m, p.tiles_n,
+                            p.group_m, GROUPED);
+  const int row0 = tc.r * BM, col0 = tc.c * BN;
+  const int rows = min(BM, p.M - row0), cols = min(BN, p.N - col0);
+  float* c = p.C + static_cast<long long>(row0) * p.ldc + col0;
+  for (int i = threadIdx.x; i < rows * cols; i += 256) {
+    float* e = c + static_cast<long long>(i / cols) * p.ldc + (i % cols);
+    *e = p.beta == 0.0f ? 0.0f : p.beta * *e;
+  }
+}
+
 template <class Cfg, bool VEC>
 __global__ void __launch_bounds__(Cfg::NT) sgemm_tile_kernel(KernelArgs p) {
   constexpr Geom g = make_geom(Cfg::tile);
@@ -395,8 +432,26 @@ __global__ void __launch_bounds__(Cfg::NT) sgemm_tile_kernel(KernelArgs p) {
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const TileRC tc = tile_of(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m,
-                            (Cfg::OPT & kOptXcdRemap) != 0);
+  constexpr bool kXcd = (Cfg::OPT & kOptXcdRemap) != 0;
+  // Whole tiles first (one workgroup each), then the K segments of the split
+  // tiles.
+  int pos = blockIdx.x, kt0 = 0, kt1 = p.nk;
+  bool split = false;
+  if constexpr ((Cfg::OPT & kOptSplitK) != 0) {
+    if (pos >= p.tiles_full) {
+      const int j = pos - p.tiles_full;
+      const int seg = j % p.splits;
+      pos = p.tiles_full + j / p.splits;
+      kt0 = split_begin(seg, p.splits, p.nk);
+      kt1 = split_begin(seg + 1, p.splits, p.nk);
+      split = true;
+    } else if (kXcd) {
+      pos = xcd_position(pos, p.tiles_full);
+    }
+  } else if (kXcd) {
+    pos = xcd_position(pos, p.tiles_m * p.tiles_n);
+  }
+  const TileRC tc = tile_at(pos, p.tiles_m, p.tiles_n, p.group_m, kXcd);
   const int row0 = tc.r * g.BM;
   const int col0 = tc.c * g.BN;
   const int wr0 = wave_row0(g, wave), wc0 = wave_col0(g, wave);
@@ -405,20 +460,19 @@ __global__ void __launch_bounds__(Cfg::NT) sgemm_tile_kernel(KernelArgs p) {
   acc_zero(acc);
 
   if constexpr ((Cfg::OPT & kOptPipelined) != 0) {
-    k_loop_pipelined<Cfg, VEC>(p, lds, row0, col0, t, wr0, wc0, lane, acc);
+    k_loop_pipelined<Cfg, VEC>(p, lds, row0, col0, t, wr0, wc0, lane, kt0, kt1, acc);
   } else {
     Staged<Cfg> s;
-    const int nk = (p.K + g.BK - 1) / g.BK;
-    stage_load<Cfg, VEC>(p, row0, col0, 0, t, s);
+    stage_load<Cfg, VEC>(p, row0, col0, kt0 * g.BK, t, s);
     stage_store<Cfg>(lds, t, s);
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const float* cur = lds + (kt & 1) * g.STAGE;
-      const bool more = kt + 1 < nk;
+    for (int kt = kt0; kt < kt1; ++kt) {
+      const float* cur = lds + ((kt - kt0) & 1) * g.STAGE;
+      const bool more = kt + 1 < kt1;
       if (more) stage_load<Cfg, VEC>(p, row0, col0, (kt + 1) * g.BK, t, s);
       if constexpr (VEC && !(Cfg::OPT & kOptFloatLoads)) __builtin_amdgcn_sched_barrier(0);  // loads stay ahead of the inner product
       inner_product<Cfg>(cur, wr0, wc0, lane, acc);
-      if (more) stage_store<Cfg>(lds + ((kt + 1) & 1) * g.STAGE, t, s);
+      if (more) stage_store<Cfg>(lds + ((kt - kt0 + 1) & 1) * g.STAGE, t, s);
       __syncthreads();
     }
   }
@@ -427,6 +481,12 @@ __global__ void __launch_bounds__(Cfg::NT) sgemm_tile_kernel(KernelArgs p) {
   const int clim = min(g.WN, p.N - col0 - wc0);
   if (rlim <= 0 || clim <= 0) return;
   float* cw = p.C + static_cast<long long>(row0 + wr0) * p.ldc + (col0 + wc0);
+  if constexpr ((Cfg::OPT & kOptSplitK) != 0) {
+    if (split) {
+      epilogue_atomic<Cfg>(cw, static_cast<int>(p.ldc), rlim, clim, lane, p.alpha, acc);
+      return;
+    }
+  }
   epilogue<Cfg, VEC>(cw, static_cast<int>(p.ldc), rlim, clim, lane, p.alpha, p.beta, acc);
 }
 
@@ -442,18 +502,49 @@ inline int xcd_group_rows(long long tiles_m, long long tiles_n, int BM, int BN) 
   return g;
 }
 
+// How a launch splits its tiles: the first tiles_full tiles run whole; the
+// rest run as `splits` K segments each.  Without the split option, or when
+// the tiles fill whole waves of `slots` concurrently resident workgroups (or
+// the last wave is at least half full), nothing is split.
+struct SplitPlan {
+  int tiles_full, splits;
+};
+
+inline SplitPlan split_plan(long long tiles, int nk, long long slots, bool enabled) {
+  if (!enabled || slots <= 0 || nk < 2) return SplitPlan{static_cast<int>(tiles), 1};
+  const long long tail = tiles % slots;
+  if (tail == 0 || 2 * tail > slots) return SplitPlan{static_cast<int>(tiles), 1};
+  long long s = slots / tail;
+  if (s > nk) s = nk;
+  if (s < 2) return SplitPlan{static_cast<int>(tiles), 1};
+  return SplitPlan{static_cast<int>(tiles - tail), static_cast<int>(s)};
+}
+
+// `slots`: workgroups of this kernel that fit on the device at once.
 template <class Cfg, bool VEC>
-hipError_t launch_tile(const KernelArgs& a, hipStream_t stream) {
+hipError_t launch_tile(const KernelArgs& a, hipStream_t stream, long long slots) {
   KernelArgs k = a;
   const long long tiles_m = (a.M + Cfg::BM - 1) / Cfg::BM;
   const long long tiles_n = (a.N + Cfg::BN - 1) / Cfg::BN;
   k.tiles_m = static_cast<int>(tiles_m);
   k.tiles_n = static_cast<int>(tiles_n);
   k.group_m = xcd_group_rows(tiles_m, tiles_n, Cfg::BM, Cfg::BN);
+  k.nk = (a.K + Cfg::BK - 1) / Cfg::BK;
+  const SplitPlan sp = split_plan(tiles_m * tiles_n, k.nk, slots, (Cfg::OPT & kOptSplitK) != 0);
+  k.tiles_full = sp.tiles_full;
+  k.splits = sp.splits;
   void* args[] = {&k};
+  const long long tail = tiles_m * tiles_n - sp.tiles_full;
+  if (sp.splits > 1 && a.beta != 1.0f) {
+    constexpr bool kGrouped = (Cfg::OPT & kOptXcdRemap) != 0;
+    const hipError_t e = hipLaunchKernel(
+        reinterpret_cast<const void*>(&sgemm_scale_tiles_kernel<Cfg::BM, Cfg::BN, kGrouped>),
+        dim3(static_cast<unsigned>(tail)), dim3(256), args, 0, stream);
+    if (e != hipSuccess) return e;
+  }
+  const long long grid = sp.tiles_full + tail * sp.splits;
   return hipLaunchKernel(reinterpret_cast<const void*>(&sgemm_tile_kernel<Cfg, VEC>),
-                         dim3(static_cast<unsigned>(tiles_m * tiles_n)), dim3(Cfg::NT), args, 0,
-                         stream);
+                         dim3(static_cast<unsigned>(grid)), dim3(Cfg::NT), args, 0, stream);
 }
 
 template <class Cfg, bool VEC>

@@ -53,7 +53,13 @@ enum Opt : int {
   // pinned to the top of the slice in the float4 variant); kept so the two
   // schedules can be compared in one process.
   kOptFloatLoads = 4,
-  kOptAll = 7,
+  // Split along K the tiles of a last, partly filled wave of workgroups (or
+  // all tiles when they do not fill one wave): their segments add alpha *
+  // partial into C with fp32 atomics after a pre-pass has scaled those tiles
+  // of C by beta.  Those tiles' sums are therefore not bitwise reproducible
+  // from run to run (they stay within the parity bound).
+  kOptSplitK = 8,
+  kOptAll = 15,
 };
 
 // Machine limits the checker enforces.

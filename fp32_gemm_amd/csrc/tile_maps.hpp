@@ -135,25 +135,42 @@ FG_HD constexpr int mfma_out_row(const Geom& g, int l, int r) {
 FG_HD constexpr int mfma_out_col(const Geom& g, int l) { return l % mfma_blk(g); }
 
 // ---- workgroup -> output tile ----------------------------------------------
-// Plain order: tile row = id / tiles_n, tile column = id % tiles_n.
-// XCD-aware order: the hardware hands consecutive workgroup ids to the 8
-// XCDs in turn, so id -> (xcd = id % 8, local = id / 8) and each XCD gets one
-// contiguous run of a grouped raster (group_m tile rows per group, walked
-// column by column), i.e. a compact block of tiles sharing few A row panels
-// and B column panels in its L2.  Both orders are bijections onto the tiles.
+// Tiles are visited in a "tile order": plain row-major, or (XCD-aware option)
+// a grouped raster with group_m tile rows per group, walked column by column
+// inside a group.  Workgroup ids map to positions in that order: directly, or
+// (XCD-aware) so that the ids the hardware hands to one of the 8 XCDs (id % 8
+// equal) get one contiguous run of positions, i.e. one compact block of tiles
+// whose A row panels and B column panels that XCD's L2 shares.  Every map
+// here is a bijection.
 struct TileRC { int r, c; };
-FG_HD constexpr TileRC tile_of(int id, int tiles_m, int tiles_n, int group_m, bool xcd) {
-  if (!xcd) return TileRC{id / tiles_n, id % tiles_n};
-  const int ntiles = tiles_m * tiles_n;
-  const int q = ntiles / 8, rem = ntiles % 8;
-  const int x = id % 8, local = id / 8;
-  const int t = x * q + (x < rem ? x : rem) + local;
+
+FG_HD constexpr TileRC tile_at(int pos, int tiles_m, int tiles_n, int group_m, bool grouped) {
+  if (!grouped) return TileRC{pos / tiles_n, pos % tiles_n};
   const int per_group = group_m * tiles_n;
-  const int grp = t / per_group;
+  const int grp = pos / per_group;
   const int first = grp * group_m;
   const int gh = (tiles_m - first) < group_m ? (tiles_m - first) : group_m;
-  const int within = t - grp * per_group;
+  const int within = pos - grp * per_group;
   return TileRC{first + within % gh, within / gh};
+}
+
+// Workgroup id in [0, count) -> position in [0, count): XCD x = id % 8 gets
+// the x-th contiguous run.
+FG_HD constexpr int xcd_position(int id, int count) {
+  const int q = count / 8, rem = count % 8;
+  const int x = id % 8, local = id / 8;
+  return x * q + (x < rem ? x : rem) + local;
+}
+
+FG_HD constexpr TileRC tile_of(int id, int tiles_m, int tiles_n, int group_m, bool xcd) {
+  return xcd ? tile_at(xcd_position(id, tiles_m * tiles_n), tiles_m, tiles_n, group_m, true)
+             : tile_at(id, tiles_m, tiles_n, group_m, false);
+}
+
+// K-slice range [first, last) of segment s when a tile's nk slices are split
+// into S segments; the segments partition [0, nk) for any 1 <= S <= nk.
+FG_HD constexpr int split_begin(int s, int S, int nk) {
+  return static_cast<int>((static_cast<long long>(s) * nk) / S);
 }
 
 // ---- output ownership (row, col within the block tile) ---------------------

@@ -59,11 +59,12 @@ def _exact_check(cfg_id, M, N, K, dev, samples=1500):
     return bool(np.array_equal(got.view(np.uint32), want.view(np.uint32)))
 
 
-def usable_configs():
+def usable_configs(vector_variant=True):
+    """Compiled configurations whose kernel for this variant does not spill."""
     out = []
     for c in fg.configs():
-        rv, rs = c["resources_vec"], c["resources_scalar"]
-        if rv is None or rs is None or rv.get("ScratchSize", 1) > 0:
+        r = c["resources_vec"] if vector_variant else c["resources_scalar"]
+        if r is None or r.get("ScratchSize", 1) > 0:
             continue
         out.append(c)
     return out
@@ -172,7 +173,7 @@ def main():
     if fg.device_check() != 0:
         raise SystemExit("tune: current device is not gfx950")
     paths = set(args.paths.split(","))
-    configs = [c for c in usable_configs() if c["path_name"] in paths]
+    configs = {v: [c for c in usable_configs(v) if c["path_name"] in paths] for v in (True, False)}
     if args.top_from:
         prev = [json.loads(l) for l in open(args.top_from)]
         keep = set()
@@ -180,9 +181,10 @@ def main():
             rs = sorted((r for r in prev if r["workload"] == wl and r.get("protocol") == "short"
                          and r["exact"]), key=lambda r: r["ms"])
             keep |= {tuple(r["tuple"]) for r in rs[:args.top]}
-        configs = [c for c in configs if tuple(c["tuple"]) in keep]
+        configs = {v: [c for c in cs if tuple(c["tuple"]) in keep] for v, cs in configs.items()}
     if args.filter:
-        configs = [c for c in configs if eval(args.filter, {}, {"c": c})]
+        configs = {v: [c for c in cs if eval(args.filter, {}, {"c": c})]
+                   for v, cs in configs.items()}
     os.makedirs(os.path.dirname(args.out) or ".", exist_ok=True)
     fout = open(args.out, "a")
 
@@ -199,7 +201,7 @@ def main():
     for name in names:
         w = inputs.WORKLOADS[name]
         t0 = time.time()
-        use = configs
+        use = configs[w.K % 4 == 0 and w.N % 4 == 0]
         if ranked is not None and model.flops(w.M, w.N, w.K) > args.prune_above:
             use = ranked[:args.keep]
         print(f"[tune] {name}: {len(use)} configs", flush=True)
@@ -207,7 +209,7 @@ def main():
         if model.flops(w.M, w.N, w.K) <= args.prune_above:
             order = sorted((r for r in results if r.get("protocol") == "short" and r["exact"]),
                            key=lambda r: r["ms"])
-            by_id = {c["id"]: c for c in configs}
+            by_id = {c["id"]: c for c in configs[True] + configs[False]}
             ranked = [by_id[r["cfg_id"]] for r in order]
         print(f"[tune] {name}: best cfg {best['cfg_id']} {best['tuple']} {best['ms']:.4f} ms "
               f"{best['tflops']:.1f} TFLOP/s ({time.time() - t0:.0f} s)", flush=True)

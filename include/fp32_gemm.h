@@ -93,7 +93,8 @@ typedef struct sgemm_config_t {
   int32_t BM, BN, BK, WM, WN, WNITER, TM, TN, NT;
   int32_t swz; /* 0 = unswizzled LDS, 32 or 64 = XOR swizzle for that bank count */
   int32_t opt; /* schedule options: bit 0 pipelined MFMA loop, bit 1 XCD-aware tile order,
-                  bit 2 unpinned global loads */
+                  bit 2 unpinned global loads, bit 3 split-K for a partly filled last wave
+                  (those tiles accumulate with fp32 atomics: not bitwise reproducible) */
   int32_t WMITER, WSUBM, WSUBN;
   int32_t acc_per_lane;
   int32_t lds_bytes;     /* both LDS stages */
@@ -109,12 +110,16 @@ int sgemm_config_info(int32_t id, sgemm_config_t* out);
 typedef struct sgemm_plan_t {
   int32_t cfg_id;
   int32_t vector_variant; /* 1 = float4 staging, 0 = scalar staging */
-  int64_t grid;           /* workgroups */
+  int64_t grid;           /* workgroups of the GEMM kernel */
   int32_t block;          /* threads per workgroup */
+  int32_t tiles_full;     /* output tiles computed whole by one workgroup */
+  int32_t splits;         /* K segments of each remaining tile (1 = none) */
 } sgemm_plan_t;
 
 /* Validates like sgemm_ex (same status codes, no device check) and fills
- * *out.  cfg_id < 0 selects the tuned configuration. */
+ * *out.  cfg_id < 0 selects the tuned configuration.  The split decision
+ * needs the device's compute-unit count; without a device it reports no
+ * split. */
 int sgemm_plan(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
                int64_t ldb, const float* C, int64_t ldc, int32_t cfg_id, sgemm_plan_t* out);
 

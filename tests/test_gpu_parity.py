@@ -133,6 +133,49 @@ def test_every_config_both_variants(fg, dev, ragged_cases, chunk):
     log(f"[parity] worst err {worst:.3e}")
 
 
+def test_split_configs_with_whole_and_split_tiles(fg, dev, orc):
+    """Every split-K configuration on a shape whose tiles overflow the
+    resident workgroups by a small tail, so whole tiles and atomically summed
+    K segments meet in one launch: integer inputs must stay bit-exact and
+    nothing outside C may change."""
+    M, N, K = 4097, 4095, 130
+    A, B, C = inputs.make_small_int(M, N, K, seed=31)
+    rows, cols = inputs.sample_indices(M, N, 2000, seed=32)
+    for r in (0, M // 2, M - 1):
+        rows = np.concatenate([rows, np.full(N, r)])
+        cols = np.concatenate([cols, np.arange(N)])
+    e32, _ = orc.entries(rows, cols, A, B, C, 0.5, 3.0)
+    seen = 0
+    for c in fg.configs():
+        if not c["opt"] & 8:
+            continue
+        for ldc_pad in (0, 3):   # vector (N % 4 != 0 -> scalar anyway) and padded
+            cv = run(fg, dev, A, B, C, 0.5, 3.0, cfg=c["id"], ldc_pad=ldc_pad, guard=1)
+            plan = fg.plan(M, N, K, 1 << 40, K, 2 << 40, N, 4 << 40, N + ldc_pad, c["id"])
+            log(f"[split] cfg {c['id']} {c['tuple']} tiles_full={plan['tiles_full']} "
+                f"splits={plan['splits']}")
+            assert cv.untouched(), f"cfg {c['id']}: wrote outside C"
+            got = cv.result()
+            assert np.array_equal(got[rows, cols].view(np.uint32), e32.view(np.uint32)), c["id"]
+            seen += plan["splits"] > 1 and plan["tiles_full"] > 0
+    assert seen > 0, "no configuration split a tail"
+
+
+def test_split_configs_random_inputs_within_tolerance(fg, dev, orc):
+    M, N, K = 1000, 1500, 777
+    A, B, C = inputs.make_random(M, N, K, seed=33)
+    _, r64 = orc.sgemm(A, B, C, 1.0, 1.0)
+    _, r64b = orc.sgemm(A, B, C, 0.5, 0.0)
+    for c in fg.configs():
+        if not c["opt"] & 8:
+            continue
+        cv = run(fg, dev, A, B, C, 1.0, 1.0, cfg=c["id"])
+        assert cv.untouched()
+        check_close(cv.result(), r64, K, A, B, f"split cfg {c['id']}")
+        cv = run(fg, dev, A, B, C, 0.5, 0.0, cfg=c["id"])
+        check_close(cv.result(), r64b, K, A, B, f"split cfg {c['id']} beta=0")
+
+
 # ---------------------------------------------------------------------------
 # The workload configurations, through the tuned dispatch.
 
