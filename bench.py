@@ -35,6 +35,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-context", action="store_true", help="skip timing torch.mm")
+    ap.add_argument("--ladder", action="store_true",
+                    help="only time the four ladder rungs on the workload (one JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -70,6 +72,40 @@ def cpu_baseline(w, A, B, C, target_s):
                       f"(fp64 accumulation, OpenMP over rows), {dt:.1f} s"}
 
 
+def ladder(fg, inputs, model, w, dev, args):
+    """Time the kernel ladder (the pages' progression rebuilt for wave64)."""
+    import numpy as np
+    import torch
+    A, B, C = inputs.make(w)
+    Ad, Bd = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+    C0 = torch.from_numpy(C).to(dev)
+    Cd = C0.clone()
+    stream = torch.cuda.current_stream(dev)
+    names = {1: "shared-memory tiling, 1 output/lane, 32x32",
+             2: "VALU 128x128x8, 8x8 per lane, A transposed, float4",
+             3: "VALU warp tiling 128x64x16, 64x64 waves, 4x4 patches",
+             4: "tuned MFMA dispatch"}
+    out = {"ladder": [], "workload": w.name}
+    flops = model.flops(w.M, w.N, w.K)
+    for rung in (1, 2, 3, 4):
+        reps = max(3, min(args.steps, 20))
+        for _ in range(2):
+            fg.ladder(rung, Ad, Bd, Cd, w.alpha, w.beta, stream=stream)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for i in range(reps):
+            fg.ladder(rung, Ad, Bd, Cd, w.alpha, w.beta, stream=stream)
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
+        out["ladder"].append({"rung": rung, "kernel": names[rung], "ms": round(ms, 4),
+                              "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                              "pct_of_peak": round(100 * flops / (ms * 1e-3) / 1e12
+                                                   / model.PEAK_FP32_TFLOPS, 2)})
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -99,6 +135,9 @@ def main():
             raise SystemExit(f"bench.py: no compiled configuration {want}")
         args.cfg = ids[0]
     w = inputs.WORKLOADS[args.workload]
+    if args.ladder:
+        ladder(fg, inputs, model, w, dev, args)
+        return
     A, B, C = inputs.make(w)
     Ad = torch.from_numpy(A).to(dev)
     Bd = torch.from_numpy(B).to(dev)

@@ -10,7 +10,7 @@ can be imported on a machine where the library has not been built.
 """
 _API = ("sgemm", "sgemm_ex", "sgemm_raw", "plan", "num_configs", "config_info", "configs",
         "status_string", "device_check", "SgemmError", "library_path", "check_tuple",
-        "simulate_tuple", "exported_symbols", "tile_order")
+        "simulate_tuple", "exported_symbols", "tile_order", "ladder")
 
 
 def __getattr__(name):

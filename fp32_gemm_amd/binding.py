@@ -56,6 +56,8 @@ _SIGS = {
     "sgemm": ([_i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64], ctypes.c_int),
     "sgemm_ex": ([_i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64, _vp, _i32],
                  ctypes.c_int),
+    "sgemm_ladder": ([_i32, _i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64, _vp],
+                     ctypes.c_int),
     "sgemm_num_configs": ([], ctypes.c_int),
     "sgemm_config_info": ([_i32, ctypes.POINTER(_Config)], ctypes.c_int),
     "sgemm_plan": ([_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i32,
@@ -237,6 +239,25 @@ def sgemm_ex(A, B, C, alpha=1.0, beta=0.0, stream=None, cfg_id=-1):
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
     with torch.cuda.device(C.device):
         rc = _lib.sgemm_ex(M, N, K, alpha, a, lda, b, ldb, beta, c, ldc, handle, cfg_id)
+    if rc != 0:
+        raise SgemmError(rc)
+    return C
+
+
+def ladder(rung, A, B, C, alpha=1.0, beta=0.0, stream=None):
+    """C <- alpha * A @ B + beta * C with the kernel of ladder rung 1-4."""
+    a, lda = _operand(A, "A")
+    b, ldb = _operand(B, "B")
+    c, ldc = _operand(C, "C")
+    M, K = A.shape
+    N = B.shape[1]
+    if B.shape[0] != K or tuple(C.shape) != (M, N):
+        raise ValueError("shape mismatch")
+    if stream is None:
+        stream = torch.cuda.current_stream(C.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    with torch.cuda.device(C.device):
+        rc = _lib.sgemm_ladder(rung, M, N, K, alpha, a, lda, b, ldb, beta, c, ldc, handle)
     if rc != 0:
         raise SgemmError(rc)
     return C

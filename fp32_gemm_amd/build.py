@@ -64,6 +64,7 @@ def candidates():
             out += [base + (0,), base + (3,)]
     # VALU outer products: wave64 analogues of the page's shapes.
     for t in [
+        (128, 128, 8, 32, 128, 1, 8, 8, 256),   # the vectorized kernel's thread map (no warp tiling)
         (128, 128, 8, 64, 64, 1, 8, 8, 256),    # the page's square 128x128 tile, 8x8 lanes
         (128, 128, 16, 64, 64, 1, 8, 8, 256),
         (128, 64, 16, 64, 64, 2, 4, 4, 128),    # the page's winning shape, WN widened for 64 lanes
@@ -76,6 +77,9 @@ def candidates():
     ]:
         out.append(t + (VALU, 32, 0))
         out.append(t + (VALU, 32, 2))
+    # The ladder's VALU rungs in the pages' unswizzled LDS layout.
+    out.append((128, 128, 8, 32, 128, 1, 8, 8, 256, VALU, 0, 0))
+    out.append((128, 64, 16, 64, 64, 2, 4, 4, 128, VALU, 0, 0))
     # Split-K of a partly filled last wave, on the shapes ragged or small
     # problems use.
     for base in [(256, 256, 32, 64, 128, 4, 16, 1, 512, MFMA32, 32),
@@ -175,7 +179,8 @@ def build(verbose=True, jobs=None):
     t_srcs = generate()
     jobs = jobs or min(16, os.cpu_count() or 4)
     api = os.path.join(CSRC, "sgemm_api.hip")
-    work = [(api, os.path.join(BUILD, "sgemm_api.o"), False)]
+    work = [(api, os.path.join(BUILD, "sgemm_api.o"), False),
+            (os.path.join(CSRC, "ladder.hip"), os.path.join(BUILD, "ladder.o"), True)]
     work += [(s, s[:-4] + ".o", True) for s in t_srcs]
     resources = {}
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:

@@ -78,6 +78,22 @@ int sgemm_ex(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64
              const float* B, int64_t ldb, float beta, float* C, int64_t ldc, void* stream,
              int32_t cfg_id);
 
+/* The same computation with the kernel of one rung of the ladder the pages
+ * climb, rebuilt for 64-lane waves (reference points, not fast paths except
+ * rung 4):
+ *   1  shared-memory tiling, one output per lane, 32 x 32 tiles, two
+ *      barriers per K step ("Shared Memory Tiling", kernel listing);
+ *   2  128 x 128 x 8 tile, 8 x 8 outputs per lane, A transposed in LDS, 128-bit
+ *      accesses ("Vectorized Memory Access: 128-bit Loads and Stores");
+ *   3  warp tiling, 128 x 64 x 16 tile, 64 x 64 wave tiles, 4 x 4 patches
+ *      ("Warp Tiling: A Third Level of Tiling");
+ *   4  the tuned dispatch of sgemm_ex (MFMA).
+ * Rungs 2-3 run compiled VALU configurations (SGEMM_ERR_BAD_CONFIG if absent);
+ * argument rules, status codes and asynchrony as sgemm_ex. */
+int sgemm_ladder(int32_t rung, int64_t M, int64_t N, int64_t K, float alpha, const float* A,
+                 int64_t lda, const float* B, int64_t ldb, float beta, float* C, int64_t ldc,
+                 void* stream);
+
 /* ---- introspection -------------------------------------------------------- */
 
 #define SGEMM_PATH_VALU 0   /* fp32 FMA outer products on the vector ALUs */

@@ -135,3 +135,20 @@ def test_default_configs_do_not_spill():
         res = [x for x in fg.configs() if x["id"] == c["id"]][0]
         assert res["resources_vec"]["ScratchSize"] == 0
         assert res["resources_scalar"]["ScratchSize"] == 0
+
+
+def test_ladder_argument_handling():
+    lib = ctypes.CDLL(fg.library_path())
+    f = lib.sgemm_ladder
+    f.argtypes = binding._SIGS["sgemm_ladder"][0]
+    f.restype = ctypes.c_int
+    # bad rung before anything else
+    assert f(0, 4, 4, 4, 1.0, FAKE, 4, FAKE * 2, 4, 0.0, FAKE * 4, 4, None) == 2
+    assert f(5, 4, 4, 4, 1.0, FAKE, 4, FAKE * 2, 4, 0.0, FAKE * 4, 4, None) == 2
+    # argument validation, same codes as sgemm_ex
+    assert f(1, -1, 4, 4, 1.0, FAKE, 4, FAKE * 2, 4, 0.0, FAKE * 4, 4, None) == -1
+    assert f(1, 4, 4, 8, 1.0, FAKE, 7, FAKE * 2, 4, 0.0, FAKE * 4, 4, None) == -6
+    assert f(1, 0, 4, 4, 1.0, FAKE, 4, FAKE * 2, 4, 0.0, FAKE * 4, 4, None) == 0
+    import torch
+    if not torch.cuda.is_available():
+        assert f(1, 4, 4, 4, 1.0, FAKE, 4, FAKE * 2, 4, 0.0, FAKE * 4, 4, None) == 1

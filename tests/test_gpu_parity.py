@@ -176,6 +176,26 @@ def test_split_configs_random_inputs_within_tolerance(fg, dev, orc):
         check_close(cv.result(), r64b, K, A, B, f"split cfg {c['id']} beta=0")
 
 
+@pytest.mark.parametrize("rung", [1, 2, 3, 4])
+def test_ladder_rungs(fg, dev, orc, rung):
+    """Each rung of the kernel ladder on ragged shapes: within tolerance on
+    random inputs, bit-exact on integer inputs, C outside M x N untouched."""
+    for (M, N, K) in [(300, 260, 200), (1000, 1500, 777), (512, 512, 512)]:
+        A, B, C = inputs.make_random(M, N, K, seed=M + rung)
+        _, r64 = orc.sgemm(A, B, C, 0.5, 3.0)
+        cv = Canvas(C, N + 5, 2, dev)
+        fg.ladder(rung, to_dev(A, dev), to_dev(B, dev), cv.view, 0.5, 3.0)
+        torch.cuda.synchronize()
+        assert cv.untouched()
+        check_close(cv.result(), r64, K, A, B, f"rung {rung} {M}x{N}x{K}")
+        Ai, Bi, Ci = inputs.make_small_int(M, N, K, seed=M + 7 * rung)
+        i32, _ = orc.sgemm(Ai, Bi, Ci, 0.5, 3.0)
+        cv = Canvas(Ci, N, 1, dev)
+        fg.ladder(rung, to_dev(Ai, dev), to_dev(Bi, dev), cv.view, 0.5, 3.0)
+        torch.cuda.synchronize()
+        assert np.array_equal(cv.result().view(np.uint32), i32.view(np.uint32)), f"rung {rung}"
+
+
 # ---------------------------------------------------------------------------
 # The workload configurations, through the tuned dispatch.
 
