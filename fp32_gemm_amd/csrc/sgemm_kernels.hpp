@@ -221,6 +221,8 @@ __device__ __forceinline__ void inner_product(const float* st, int wr0, int wc0,
               float& a = acc.v[valu_acc_index(g, wm, i, wn, j)];
               a = __builtin_fmaf(rm[b][wm * g.TM + i], rn[b][wn * g.TN + j], a);
             }
+      // Keep k-steps apart: LDS reads of later steps may not move above the
+      // FMAs of this one (which would need BK sets of fragment registers).
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
@@ -466,13 +468,17 @@ __global__ void __launch_bounds__(Cfg::NT) sgemm_tile_kernel(KernelArgs p) {
     stage_load<Cfg, VEC>(p, row0, col0, kt0 * g.BK, t, s);
     stage_store<Cfg>(lds, t, s);
     __syncthreads();
+    // Branch-free body: on the last slice the load reads nothing useful (past
+    // K every element is masked; at a segment end it is the next segment's
+    // slice) and the store lands in the stage no one reads again.  A branch
+    // here would let the compiler sink the whole inner product's arithmetic
+    // below it, away from its LDS reads.
     for (int kt = kt0; kt < kt1; ++kt) {
       const float* cur = lds + ((kt - kt0) & 1) * g.STAGE;
-      const bool more = kt + 1 < kt1;
-      if (more) stage_load<Cfg, VEC>(p, row0, col0, (kt + 1) * g.BK, t, s);
+      stage_load<Cfg, VEC>(p, row0, col0, (kt + 1) * g.BK, t, s);
       if constexpr (VEC && !(Cfg::OPT & kOptFloatLoads)) __builtin_amdgcn_sched_barrier(0);  // loads stay ahead of the inner product
       inner_product<Cfg>(cur, wr0, wc0, lane, acc);
-      if (more) stage_store<Cfg>(lds + ((kt - kt0 + 1) & 1) * g.STAGE, t, s);
+      stage_store<Cfg>(lds + ((kt - kt0 + 1) & 1) * g.STAGE, t, s);
       __syncthreads();
     }
   }
