@@ -49,7 +49,8 @@ class _Attr(ctypes.Structure):
 
 class _SimReport(ctypes.Structure):
     _fields_ = [("failed_check", _i32), ("store_a_ways", _i32), ("store_b_ways", _i32),
-                ("read_a_ways", _i32), ("read_b_ways", _i32)]
+                ("read_a_ways", _i32), ("read_b_ways", _i32), ("dma_read_a_ways", _i32),
+                ("dma_read_b_ways", _i32)]
 
 
 _SIGS = {

@@ -98,6 +98,21 @@ def candidates():
                  (128, 128, 32, 32, 64, 2, 16, 1, 512, MFMA32, 32),
                  (256, 256, 16, 64, 128, 4, 16, 1, 512, MFMA32, 32)]:
         out += [base + (4,), base + (7,)]
+    # Direct global-to-LDS staging (MFMA 32x32x2), plain and XCD-aware.
+    for BM, BN in [(256, 256), (256, 128), (128, 256), (128, 128)]:
+        for BK in (16, 32, 64):
+            for WM in (32, 64, 128):
+                for WN in (32, 64, 128):
+                    if WM > BM or WN > BN or (BM // WM) * (BN // WN) not in (4, 8):
+                        continue
+                    base = (BM, BN, BK, WM, WN, WN // 32, 16, 1, 64 * (BM // WM) * (BN // WN),
+                            MFMA32, 32)
+                    out += [base + (16,), base + (18,)]
+    for base in [(256, 256, 32, 64, 128, 4, 16, 1, 512, MFMA32, 32),
+                 (256, 256, 32, 128, 64, 2, 16, 1, 512, MFMA32, 32),
+                 (128, 128, 32, 32, 64, 2, 16, 1, 512, MFMA32, 32),
+                 (128, 128, 32, 64, 64, 2, 16, 1, 256, MFMA32, 32)]:
+        out += [base + (20,), base + (24,), base + (26,)]
     # Bank-model variants of the headline shapes: unswizzled, and 64 banks.
     for base in [(256, 256, 16, 128, 128, 4, 16, 1, 256, MFMA32),
                  (256, 256, 32, 128, 128, 4, 16, 1, 256, MFMA32),

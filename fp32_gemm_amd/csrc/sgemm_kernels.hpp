@@ -18,6 +18,10 @@
 // its last use (the page "Shared Memory Tiling" explains why a single buffer
 // needs a barrier on both sides of the inner product).
 //
+// With the direct-LDS option (MFMA 32x32x2, float4 variant) the loads of
+// slice kt+1 write the other LDS stage themselves: no staging registers and no
+// LDS stores; each wave waits for its own loads (vmcnt) before the barrier.
+//
 // Operands are read through buffer resources rebuilt per slice, so every load
 // is range-checked by the hardware; elements outside the logical M x K and
 // K x N windows are masked by giving them an offset past the resource's end,
@@ -71,6 +75,16 @@ __device__ __forceinline__ f32x4 buffer_load4(__amdgpu_buffer_rsrc_t r, int off)
 
 __device__ __forceinline__ float buffer_load1(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r, int off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
+}
+
+__device__ __forceinline__ void buffer_store1(__amdgpu_buffer_rsrc_t r, int off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, off, 0, 0);
 }
 
 template <class Cfg>
@@ -140,6 +154,75 @@ __device__ __forceinline__ void stage_store(float* stage, int t, const Staged<Cf
     *reinterpret_cast<f32x4*>(&stage[bs_index(g, k, c)]) = s.b[ps];
   }
 }
+
+// ---- direct-LDS staging --------------------------------------------------
+
+// LDS (address space 3) pointer; a C-style cast from a generic pointer into
+// a __shared__ array is an address-space cast.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Per-lane part of each of this wave's direct-LDS instructions that does not
+// change from slice to slice: the byte offset from the slice origin
+// (A[row0][k0] or B[k0][col0]; kMaskedOffset for rows of A past M and columns
+// of B past N), and the in-slice k the lane's float4 starts at, which decides
+// whether it lies inside K on a given slice.
+template <class Cfg>
+struct DmaLanes {
+  static constexpr Geom g = make_geom(Cfg::tile);
+  int a_off[dma_ops_a(g)], a_k[dma_ops_a(g)];
+  int b_off[dma_ops_b(g)], b_k[dma_ops_b(g)];
+};
+
+template <class Cfg>
+__device__ __forceinline__ void dma_setup(const KernelArgs& p, int row0, int col0, int wave,
+                                          int lane, DmaLanes<Cfg>& d) {
+  constexpr Geom g = make_geom(Cfg::tile);
+  const int lda = static_cast<int>(p.lda), ldb = static_cast<int>(p.ldb);
+  const int rows = p.M - row0, cols = p.N - col0;
+#pragma unroll
+  for (int j = 0; j < dma_ops_a(g); ++j) {
+    const MK s = dma_a_src(g, dma_op(g, wave, j), lane);
+    d.a_off[j] = s.m < rows ? (s.m * lda + 4 * s.kq) * 4 : kMaskedOffset;
+    d.a_k[j] = 4 * s.kq;
+  }
+#pragma unroll
+  for (int j = 0; j < dma_ops_b(g); ++j) {
+    const KN s = dma_b_src(g, dma_op(g, wave, j), lane);
+    d.b_off[j] = s.n < cols ? (s.k * ldb + s.n) * 4 : kMaskedOffset;
+    d.b_k[j] = s.k;
+  }
+}
+
+// Issue the direct-LDS loads of the slice starting at k0 into `stage`.  The
+// float4 variant's alignment guarantees (K % 4 == 0) keep every float4 wholly
+// inside or outside K.  Completion is waited for with vmcnt before the barrier
+// that publishes the stage.
+template <class Cfg>
+__device__ __forceinline__ void dma_slice(const KernelArgs& p, const DmaLanes<Cfg>& d,
+                                          float* stage, int row0, int col0, int k0, int wave) {
+  constexpr Geom g = make_geom(Cfg::tile);
+  const int kr = p.K - k0;
+  const int rows = min(g.BM, p.M - row0);
+  const auto ra = make_rsrc(p.A + static_cast<long long>(row0) * p.lda + k0,
+                            (static_cast<long long>(rows - 1) * p.lda + kr) * 4);
+#pragma unroll
+  for (int j = 0; j < dma_ops_a(g); ++j) {
+    float* dst = stage + dma_op(g, wave, j) * 256;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(dst), 16,
+                                             d.a_k[j] < kr ? d.a_off[j] : kMaskedOffset, 0, 0, 0);
+  }
+  const int krows = min(g.BK, kr);
+  const auto rb = make_rsrc(p.B + static_cast<long long>(k0) * p.ldb + col0,
+                            (static_cast<long long>(krows - 1) * p.ldb + (p.N - col0)) * 4);
+#pragma unroll
+  for (int j = 0; j < dma_ops_b(g); ++j) {
+    float* dst = stage + g.BM * g.BK + dma_op(g, wave, j) * 256;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(dst), 16,
+                                             d.b_k[j] < kr ? d.b_off[j] : kMaskedOffset, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // ---------------------------------------------------------------------------
 // Accumulator storage and the inner product, per path.
@@ -249,6 +332,35 @@ __device__ __forceinline__ void inner_product(const float* st, int wr0, int wc0,
   }
 }
 
+// One BK slice of the MFMA 32x32x2 inner product over a direct-LDS stage:
+// per 8-k group, one 128-bit As read per sub-tile row feeds four MFMAs
+// (k = 8*kg + 4*slot + q in MFMA q), each with its own 32-bit Bs reads.
+template <class Cfg>
+__device__ __forceinline__ void inner_product_dma(const float* st, int wr0, int wc0, int lane,
+                                                  Acc<Cfg>& acc) {
+  constexpr Geom g = make_geom(Cfg::tile);
+  const int fr = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int kg = 0; kg < g.BK / 8; ++kg) {
+    f32x4 a[g.WMITER];
+    float b[4][g.WNITER];
+#pragma unroll
+    for (int wm = 0; wm < g.WMITER; ++wm)
+      a[wm] = *reinterpret_cast<const f32x4*>(&st[dma_as_index(g, wr0 + wm * 32 + fr, dma_k(kg, h, 0))]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int wn = 0; wn < g.WNITER; ++wn) b[q][wn] = st[bs_index(g, dma_k(kg, h, q), wc0 + wn * 32 + fr)];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int wm = 0; wm < g.WMITER; ++wm)
+#pragma unroll
+        for (int wn = 0; wn < g.WNITER; ++wn)
+          acc.v[wm][wn] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[wm][q], b[q][wn], acc.v[wm][wn], 0, 0, 0);
+  }
+}
+
 // ---- pipelined MFMA loop pieces ---------------------------------------------
 
 template <class Cfg>
@@ -327,51 +439,69 @@ __device__ __forceinline__ void k_loop_pipelined(const KernelArgs& p, float* lds
   }
 }
 
-__device__ __forceinline__ void update_one(float* c, float acc, float alpha, float beta) {
-  float v = alpha * acc;
-  if (beta != 0.0f) v = __builtin_fmaf(beta, *c, v);
-  *c = v;
-}
-
 // C = alpha*acc + beta*C for in-range elements.  When beta == 0 the old C is
-// not read.  `cw` points at C[row0 + wr0][col0 + wc0]; rlim/clim are the rows
-// and columns of the wave tile that lie inside M x N.
+// not read.  `cw` points at C[row0 + wr0][col0 + wc0]; rlim/clim (both >= 1)
+// are the rows and columns of the wave tile that lie inside M x N.  One
+// buffer resource spans the in-range extent of the wave tile; an element
+// outside the window gets kMaskedOffset, so its load reads zero and its store
+// is dropped by the hardware's range check (the columns between N and ldc are
+// never written).  The body has no per-element branches, and each chunk (one
+// MFMA block, or one row of VALU patches) issues all its loads of C before its
+// stores, so a wave waits for memory once per chunk rather than once per
+// element.
 template <class Cfg, bool VEC>
 __device__ __forceinline__ void epilogue(float* cw, int ldc, int rlim, int clim, int lane,
                                          float alpha, float beta, const Acc<Cfg>& acc) {
   constexpr Geom g = make_geom(Cfg::tile);
+  const auto rc = make_rsrc(cw, (static_cast<long long>(rlim - 1) * ldc + clim) * 4);
   if constexpr (Cfg::PATH == kPathValu) {
+    constexpr int V = VEC ? 4 : 1;  // floats per access
+    constexpr int PER = g.TM * g.WNITER * g.TN / V;
 #pragma unroll
-    for (int wm = 0; wm < g.WMITER; ++wm)
+    for (int wm = 0; wm < g.WMITER; ++wm) {
+      int off[PER];
 #pragma unroll
-      for (int i = 0; i < g.TM; ++i) {
-        const int r = valu_m(g, lane, wm, i);
-        if (r >= rlim) continue;
+      for (int i = 0; i < g.TM; ++i)
 #pragma unroll
         for (int wn = 0; wn < g.WNITER; ++wn)
 #pragma unroll
-          for (int j = 0; j < g.TN; j += 4) {
-            const int c = valu_n(g, lane, wn, j);
-            float* cp = cw + r * ldc + c;
-            const int e = valu_acc_index(g, wm, i, wn, j);
-            if constexpr (VEC) {
-              if (c < clim) {  // N % 4 == 0: the float4 is wholly inside or outside
-                f32x4 v = {alpha * acc.v[e], alpha * acc.v[e + 1], alpha * acc.v[e + 2],
-                           alpha * acc.v[e + 3]};
-                if (beta != 0.0f) {
-                  const f32x4 old = *reinterpret_cast<const f32x4*>(cp);
-#pragma unroll
-                  for (int q = 0; q < 4; ++q) v[q] = __builtin_fmaf(beta, old[q], v[q]);
-                }
-                *reinterpret_cast<f32x4*>(cp) = v;
-              }
-            } else {
-#pragma unroll
-              for (int q = 0; q < 4; ++q)
-                if (c + q < clim) update_one(cp + q, acc.v[e + q], alpha, beta);
-            }
+          for (int j = 0; j < g.TN; j += V) {
+            const int r = valu_m(g, lane, wm, i), c = valu_n(g, lane, wn, j);
+            // N % 4 == 0 in the float4 variant: a float4 is wholly inside or outside.
+            off[(i * g.WNITER * g.TN + wn * g.TN + j) / V] =
+                (r < rlim && c < clim) ? (r * ldc + c) * 4 : kMaskedOffset;
           }
+      float old[PER][V];
+      if (beta != 0.0f) {
+#pragma unroll
+        for (int x = 0; x < PER; ++x) {
+          if constexpr (VEC) {
+            const f32x4 o = buffer_load4(rc, off[x]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) old[x][q] = o[q];
+          } else {
+            old[x][0] = buffer_load1(rc, off[x]);
+          }
+        }
       }
+#pragma unroll
+      for (int i = 0; i < g.TM; ++i)
+#pragma unroll
+        for (int wn = 0; wn < g.WNITER; ++wn)
+#pragma unroll
+          for (int j = 0; j < g.TN; j += V) {
+            const int x = (i * g.WNITER * g.TN + wn * g.TN + j) / V;
+            const int e = valu_acc_index(g, wm, i, wn, j);
+            f32x4 v;
+#pragma unroll
+            for (int q = 0; q < V; ++q) {
+              v[q] = alpha * acc.v[e + q];
+              if (beta != 0.0f) v[q] = __builtin_fmaf(beta, old[x][q], v[q]);
+            }
+            if constexpr (VEC) buffer_store4(rc, off[x], v);
+            else buffer_store1(rc, off[x], v[0]);
+          }
+    }
   } else {
     constexpr int blk = mfma_blk(g), regs = mfma_regs(g);
     const int c_l = mfma_out_col(g, lane);
@@ -379,12 +509,23 @@ __device__ __forceinline__ void epilogue(float* cw, int ldc, int rlim, int clim,
     for (int wm = 0; wm < g.WMITER; ++wm)
 #pragma unroll
       for (int wn = 0; wn < g.WNITER; ++wn) {
+        int off[regs];
         const int c = wn * blk + c_l;
-        if (c >= clim) continue;
 #pragma unroll
         for (int r = 0; r < regs; ++r) {
           const int row = wm * blk + mfma_out_row(g, lane, r);
-          if (row < rlim) update_one(cw + row * ldc + c, acc.v[wm][wn][r], alpha, beta);
+          off[r] = (row < rlim && c < clim) ? (row * ldc + c) * 4 : kMaskedOffset;
+        }
+        float old[regs];
+        if (beta != 0.0f) {
+#pragma unroll
+          for (int r = 0; r < regs; ++r) old[r] = buffer_load1(rc, off[r]);
+        }
+#pragma unroll
+        for (int r = 0; r < regs; ++r) {
+          float v = alpha * acc.v[wm][wn][r];
+          if (beta != 0.0f) v = __builtin_fmaf(beta, old[r], v);
+          buffer_store1(rc, off[r], v);
         }
       }
   }
@@ -461,7 +602,25 @@ __global__ void __launch_bounds__(Cfg::NT) sgemm_tile_kernel(KernelArgs p) {
   Acc<Cfg> acc;
   acc_zero(acc);
 
-  if constexpr ((Cfg::OPT & kOptPipelined) != 0) {
+  if constexpr (VEC && (Cfg::OPT & kOptDirectLds) != 0) {
+    // Direct-LDS staging: slice kt+1 streams into the other stage while
+    // slice kt is multiplied; each wave waits for its own loads, and the
+    // barrier then publishes the whole stage.  The last iteration's loads are
+    // masked past K (they write zeros into the stage no one reads again).
+    DmaLanes<Cfg> d;
+    dma_setup<Cfg>(p, row0, col0, wave, lane, d);
+    dma_slice<Cfg>(p, d, lds, row0, col0, kt0 * g.BK, wave);
+    wait_vmem();
+    __syncthreads();
+    for (int kt = kt0; kt < kt1; ++kt) {
+      const float* cur = lds + ((kt - kt0) & 1) * g.STAGE;
+      dma_slice<Cfg>(p, d, lds + ((kt - kt0 + 1) & 1) * g.STAGE, row0, col0, (kt + 1) * g.BK, wave);
+      if constexpr (!(Cfg::OPT & kOptFloatLoads)) __builtin_amdgcn_sched_barrier(0);
+      inner_product_dma<Cfg>(cur, wr0, wc0, lane, acc);
+      wait_vmem();
+      __syncthreads();
+    }
+  } else if constexpr ((Cfg::OPT & kOptPipelined) != 0) {
     k_loop_pipelined<Cfg, VEC>(p, lds, row0, col0, t, wr0, wc0, lane, kt0, kt1, acc);
   } else {
     Staged<Cfg> s;

@@ -59,7 +59,13 @@ enum Opt : int {
   // of C by beta.  Those tiles' sums are therefore not bitwise reproducible
   // from run to run (they stay within the parity bound).
   kOptSplitK = 8,
-  kOptAll = 15,
+  // MFMA 32x32x2, float4 variant: global -> LDS with buffer loads that write
+  // LDS directly (no register round-trip, no ds_write), into an As[m][k]
+  // layout whose 16-byte chunks are XOR-swizzled by row; the inner product
+  // reads four k of A per 128-bit LDS read.  The scalar variant of such a
+  // tuple keeps the register-staged As[k][m] path.
+  kOptDirectLds = 16,
+  kOptAll = 31,
 };
 
 // Machine limits the checker enforces.
@@ -103,7 +109,9 @@ enum Reason : int {
   kSwizzleRange = 16,       // swizzle needs BM, BN multiples of swz, BK <= swz, BK/4 a power of 2
   kRegisterEstimate = 17,   // estimated registers over the per-lane budget
   kNoMfmaOnTarget = 18,
-  kBadOptions = 19,         // unknown option bits, or pipelining without an even k-step count
+  kBadOptions = 19,         // unknown option bits, pipelining without an even k-step count, or
+                            // direct-LDS staging on another path, with pipelining, or without
+                            // BK in {8, 16, 32, 64}
   kNumReasons = 20,
 };
 
@@ -144,6 +152,8 @@ constexpr int vgpr_estimate(const Tile& t, int wave) {
   }
   // MFMA: fragments are one register per (sub-tile row or column, k-step);
   // accumulators live in AccVGPRs.
+  // (With direct-LDS staging the float4 variant needs fewer registers than
+  // this; the scalar variant of the same tuple stages through registers.)
   const int ksteps = (t.path == kPathMfma32) ? 2 : 1;
   return 2 * ksteps * (wmiter + t.WNITER) + prefetch_regs(t) + fixed;
 }
@@ -204,6 +214,13 @@ constexpr int check_tile(const Tile& t, const Target& m) {
   } else if (t.opt & kOptPipelined) {
     return kBadOptions;
   }
+  // Direct-LDS staging: MFMA 32x32x2 only, its own loop (not the pipelined
+  // one), whole 8-k groups per slice and a power-of-two number of 16-byte
+  // chunks per As row (the chunk swizzle is an XOR below that count).
+  if ((t.opt & kOptDirectLds) &&
+      (t.path != kPathMfma32 || (t.opt & kOptPipelined) ||
+       (t.BK != 8 && t.BK != 16 && t.BK != 32 && t.BK != 64)))
+    return kBadOptions;
 
   if (m.gfx950_rules) {
     // The As/Bs XOR swizzle flips bits below swz, in steps of at least 4

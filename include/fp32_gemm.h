@@ -110,7 +110,8 @@ typedef struct sgemm_config_t {
   int32_t swz; /* 0 = unswizzled LDS, 32 or 64 = XOR swizzle for that bank count */
   int32_t opt; /* schedule options: bit 0 pipelined MFMA loop, bit 1 XCD-aware tile order,
                   bit 2 unpinned global loads, bit 3 split-K for a partly filled last wave
-                  (those tiles accumulate with fp32 atomics: not bitwise reproducible) */
+                  (those tiles accumulate with fp32 atomics: not bitwise reproducible),
+                  bit 4 direct global-to-LDS loads in the float4 variant (MFMA 32x32x2) */
   int32_t WMITER, WSUBM, WSUBN;
   int32_t acc_per_lane;
   int32_t lds_bytes;     /* both LDS stages */
@@ -184,14 +185,20 @@ int sgemm_check_tuple(const int32_t tuple[12], int32_t target);
  * every fragment read returns the element its accumulator needs, and each
  * accumulator sees every k of a slice exactly once.  Also reports the LDS
  * bank-conflict degree of each access class under a banks-wide model
- * (32 or 64 four-byte banks).  Returns 0 when all checks pass, the checker's
- * reason code if the tuple is illegal, or 100+n for failed check n. */
+ * (32 or 64 four-byte banks).  For tuples with the direct-LDS option it
+ * also checks that layout (checks 6-8: the direct loads fill each stage
+ * exactly once where the layout expects each float4, and the 8-k-group
+ * fragment reads feed every accumulator each k once).  Returns 0 when all
+ * checks pass, the checker's reason code if the tuple is illegal, or 100+n
+ * for failed check n. */
 typedef struct sgemm_sim_report_t {
   int32_t failed_check;   /* 0 = all passed */
   int32_t store_a_ways;   /* transposed A store, ds_write_b32 */
   int32_t store_b_ways;   /* B store, ds_write_b128 */
   int32_t read_a_ways;    /* fragment reads of As */
   int32_t read_b_ways;    /* fragment reads of Bs */
+  int32_t dma_read_a_ways; /* direct-LDS option: 128-bit As[m][k] reads (0 without it) */
+  int32_t dma_read_b_ways; /* direct-LDS option: Bs reads (0 without it) */
 } sgemm_sim_report_t;
 int sgemm_simulate_tuple(const int32_t tuple[12], int32_t banks, sgemm_sim_report_t* out);
 

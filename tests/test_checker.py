@@ -163,8 +163,32 @@ def test_option_guard():
     # Pipelining is an MFMA-loop option and needs an even number of k-steps.
     assert fg.check_tuple((128, 64, 16, 64, 64, 2, 4, 4, 128, VALU, 32, 1)) == 19
     assert fg.check_tuple((128, 128, 4, 128, 64, 4, 4, 1, 128, MFMA16, 0, 1)) == 19
-    assert fg.check_tuple((128, 128, 16, 64, 64, 2, 16, 1, 256, MFMA32, 32, 16)) == 19
+    assert fg.check_tuple((128, 128, 16, 64, 64, 2, 16, 1, 256, MFMA32, 32, 32)) == 19
     assert fg.check_tuple((128, 128, 16, 64, 64, 2, 16, 1, 256, MFMA32, 32, 3)) == 0
+    # Direct-LDS staging: MFMA 32x32x2 only, not with the pipelined loop, and
+    # BK a power of two from 8 to 64.
+    assert fg.check_tuple((128, 128, 16, 64, 64, 2, 16, 1, 256, MFMA32, 32, 16)) == 0
+    assert fg.check_tuple((128, 128, 16, 64, 64, 2, 16, 1, 256, MFMA32, 32, 17)) == 19
+    assert fg.check_tuple((128, 128, 16, 64, 64, 4, 4, 1, 256, MFMA16, 32, 16)) == 19
+    assert fg.check_tuple((128, 64, 16, 64, 64, 2, 4, 4, 128, VALU, 32, 16)) == 19
+    assert fg.check_tuple((96, 64, 24, 32, 64, 2, 16, 1, 192, MFMA32, 0, 16)) == 19
+    assert fg.check_tuple((96, 64, 24, 32, 64, 2, 16, 1, 192, MFMA32, 0, 0)) == 0
+
+
+def test_direct_lds_layout_is_conflict_free():
+    # The As[m][k] chunk swizzle keeps 128-bit fragment reads free of bank
+    # conflicts under both bank models; without it every phase of the read
+    # would hit one bank group (8 or 16 rows at the same chunk).
+    for t in [(256, 256, 32, 64, 128, 4, 16, 1, 512, MFMA32, 32, 16),
+              (128, 128, 16, 32, 64, 2, 16, 1, 512, MFMA32, 32, 16),
+              (128, 128, 8, 64, 64, 2, 16, 1, 256, MFMA32, 32, 16)]:
+        if fg.check_tuple(t) != 0:
+            continue
+        for banks in (32, 64):
+            r = fg.simulate_tuple(t, banks=banks)
+            assert r["status"] == 0, (t, banks, r)
+            assert r["dma_read_a_ways"] == 1, (t, banks, r)
+            assert r["dma_read_b_ways"] == (1 if banks == 32 else 2)
 
 
 @pytest.mark.parametrize("M,N", [(4096, 4096), (4097, 4095), (8192, 2048), (1000, 1500), (256, 256),
