@@ -113,6 +113,34 @@ def candidates():
                  (128, 128, 32, 32, 64, 2, 16, 1, 512, MFMA32, 32),
                  (128, 128, 32, 64, 64, 2, 16, 1, 256, MFMA32, 32)]:
         out += [base + (20,), base + (24,), base + (26,)]
+    # Direct-LDS stage rings of 3 and 4 stages (opt field 32 / 64).
+    for base in [(256, 256, 16, 128, 64, 2, 16, 1, 512, MFMA32, 32),
+                 (256, 256, 16, 64, 128, 4, 16, 1, 512, MFMA32, 32),
+                 (256, 128, 16, 128, 32, 1, 16, 1, 512, MFMA32, 32),
+                 (128, 256, 16, 128, 32, 1, 16, 1, 512, MFMA32, 32),
+                 (128, 256, 16, 64, 64, 2, 16, 1, 512, MFMA32, 32),
+                 (128, 256, 32, 128, 32, 1, 16, 1, 512, MFMA32, 32),
+                 (128, 128, 32, 64, 32, 1, 16, 1, 512, MFMA32, 32),
+                 (128, 128, 32, 32, 64, 2, 16, 1, 512, MFMA32, 32),
+                 (128, 128, 32, 128, 32, 1, 16, 1, 256, MFMA32, 32),
+                 (128, 128, 16, 64, 32, 1, 16, 1, 512, MFMA32, 32)]:
+        for ring in (32, 64):
+            out += [base + (16 | ring,), base + (18 | ring,)]
+    # Residency requests (opt field 128 * b: b + 1 workgroups per CU) on tiles
+    # whose occupancy the compiler's register use limits.
+    for t in [(128, 128, 16, 32, 64, 2, 16, 1, 512, MFMA32, 32, 16),
+              (128, 128, 16, 64, 32, 1, 16, 1, 512, MFMA32, 32, 16),
+              (128, 128, 32, 64, 32, 1, 16, 1, 512, MFMA32, 32, 18),
+              (128, 128, 32, 128, 32, 1, 16, 1, 256, MFMA32, 32, 16),
+              (128, 256, 16, 128, 32, 1, 16, 1, 512, MFMA32, 32, 16),
+              (128, 128, 32, 32, 64, 2, 16, 1, 512, MFMA32, 32, 7),
+              (64, 64, 32, 32, 32, 1, 16, 1, 256, MFMA32, 32, 0),
+              (64, 64, 16, 32, 32, 1, 16, 1, 256, MFMA32, 32, 0),
+              (128, 128, 16, 64, 64, 1, 8, 8, 256, VALU, 32, 0),
+              (128, 64, 16, 64, 64, 2, 4, 4, 128, VALU, 32, 0),
+              (128, 128, 16, 64, 64, 2, 4, 4, 256, VALU, 32, 0)]:
+        for b in (1, 2, 3):
+            out.append(t[:11] + (t[11] | (b << 7),))
     # Bank-model variants of the headline shapes: unswizzled, and 64 banks.
     for base in [(256, 256, 16, 128, 128, 4, 16, 1, 256, MFMA32),
                  (256, 256, 32, 128, 128, 4, 16, 1, 256, MFMA32),

@@ -222,7 +222,23 @@ __device__ __forceinline__ void dma_slice(const KernelArgs& p, const DmaLanes<Cf
   }
 }
 
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N of this wave's vector memory operations are
+// outstanding (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
+
+// Workgroup barrier of the direct-LDS ring: this wave's loads older than its
+// N most recent have landed in LDS and its own LDS reads have completed, then
+// every wave meets.  __syncthreads() would add a workgroup fence, which also
+// drains the N loads meant to stay in flight; the explicit waits are what the
+// stage hand-over needs, and the memory clobbers keep the compiler from
+// moving LDS accesses across the barrier.
+template <int N>
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" :: "n"(N) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // ---------------------------------------------------------------------------
 // Accumulator storage and the inner product, per path.
@@ -566,11 +582,14 @@ __global__ void __launch_bounds__(256) sgemm_scale_tiles_kernel(KernelArgs p) {
   }
 }
 
+// The body of the tile kernel (one workgroup, one output tile or K segment).
 template <class Cfg, bool VEC>
-__global__ void __launch_bounds__(Cfg::NT) sgemm_tile_kernel(KernelArgs p) {
+__device__ __forceinline__ void tile_body(const KernelArgs& p) {
   constexpr Geom g = make_geom(Cfg::tile);
   static_assert(tile_legal(Cfg::tile), "illegal tile tuple instantiated");
-  __shared__ __attribute__((aligned(16))) float lds[2 * g.STAGE];
+  constexpr bool kDirect = VEC && (Cfg::OPT & kOptDirectLds) != 0;
+  constexpr int kStages = kDirect ? stages_of(Cfg::tile) : 2;
+  __shared__ __attribute__((aligned(16))) float lds[kStages * g.STAGE];
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -602,24 +621,34 @@ __global__ void __launch_bounds__(Cfg::NT) sgemm_tile_kernel(KernelArgs p) {
   Acc<Cfg> acc;
   acc_zero(acc);
 
-  if constexpr (VEC && (Cfg::OPT & kOptDirectLds) != 0) {
-    // Direct-LDS staging: slice kt+1 streams into the other stage while
-    // slice kt is multiplied; each wave waits for its own loads, and the
-    // barrier then publishes the whole stage.  The last iteration's loads are
-    // masked past K (they write zeros into the stage no one reads again).
+  if constexpr (kDirect) {
+    // Direct-LDS staging over a ring of S stages: slice kt+S-1 streams into
+    // its stage while slice kt is multiplied.  Before each barrier a wave
+    // waits until its loads of slice kt+1 have landed (the S-2 newer slices'
+    // loads may stay in flight); the barrier then publishes that stage to
+    // every wave and also guarantees that the stage the next iteration loads
+    // into (read in this iteration) is no longer read by anyone.  Loads past
+    // the end of K are masked (they write zeros into stages no one reads
+    // again); past a segment's end they read the next segment's slices.
+    constexpr int S = kStages;
+    constexpr int kInFlight = (S - 2) * dma_ops_per_slice(Cfg::tile);
     DmaLanes<Cfg> d;
     dma_setup<Cfg>(p, row0, col0, wave, lane, d);
-    dma_slice<Cfg>(p, d, lds, row0, col0, kt0 * g.BK, wave);
-    wait_vmem();
-    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < S - 1; ++i)
+      dma_slice<Cfg>(p, d, lds + i * g.STAGE, row0, col0, (kt0 + i) * g.BK, wave);
+    ring_barrier<kInFlight>();
+    int cur = 0, nxt = S - 1;
     for (int kt = kt0; kt < kt1; ++kt) {
-      const float* cur = lds + ((kt - kt0) & 1) * g.STAGE;
-      dma_slice<Cfg>(p, d, lds + ((kt - kt0 + 1) & 1) * g.STAGE, row0, col0, (kt + 1) * g.BK, wave);
+      dma_slice<Cfg>(p, d, lds + nxt * g.STAGE, row0, col0, (kt + S - 1) * g.BK, wave);
       if constexpr (!(Cfg::OPT & kOptFloatLoads)) __builtin_amdgcn_sched_barrier(0);
-      inner_product_dma<Cfg>(cur, wr0, wc0, lane, acc);
-      wait_vmem();
-      __syncthreads();
+      inner_product_dma<Cfg>(lds + cur * g.STAGE, wr0, wc0, lane, acc);
+      ring_barrier<kInFlight>();
+      cur = cur + 1 == S ? 0 : cur + 1;
+      nxt = nxt + 1 == S ? 0 : nxt + 1;
     }
+    // Nothing may still be writing this workgroup's LDS when its waves end.
+    if constexpr (kInFlight > 0) wait_vmem<0>();
   } else if constexpr ((Cfg::OPT & kOptPipelined) != 0) {
     k_loop_pipelined<Cfg, VEC>(p, lds, row0, col0, t, wr0, wc0, lane, kt0, kt1, acc);
   } else {
@@ -653,6 +682,29 @@ __global__ void __launch_bounds__(Cfg::NT) sgemm_tile_kernel(KernelArgs p) {
     }
   }
   epilogue<Cfg, VEC>(cw, static_cast<int>(p.ldc), rlim, clim, lane, p.alpha, p.beta, acc);
+}
+
+template <class Cfg, bool VEC>
+__global__ void __launch_bounds__(Cfg::NT) sgemm_tile_kernel(KernelArgs p) {
+  tile_body<Cfg, VEC>(p);
+}
+
+// The same kernel for tuples with a residency request: the register budget is
+// capped so that waves_per_eu_of(tile) waves fit each SIMD.  A separate
+// template leaves the code generation of every other tuple untouched.
+template <class Cfg, bool VEC>
+__global__ void __launch_bounds__(Cfg::NT)
+    __attribute__((amdgpu_waves_per_eu(waves_per_eu_of(Cfg::tile))))
+    sgemm_tile_kernel_occ(KernelArgs p) {
+  tile_body<Cfg, VEC>(p);
+}
+
+template <class Cfg, bool VEC>
+const void* kernel_symbol() {
+  if constexpr (min_blocks_of(Cfg::tile) > 0)
+    return reinterpret_cast<const void*>(&sgemm_tile_kernel_occ<Cfg, VEC>);
+  else
+    return reinterpret_cast<const void*>(&sgemm_tile_kernel<Cfg, VEC>);
 }
 
 // Host-side launcher for one instantiated tuple and variant.
@@ -708,13 +760,8 @@ hipError_t launch_tile(const KernelArgs& a, hipStream_t stream, long long slots)
     if (e != hipSuccess) return e;
   }
   const long long grid = sp.tiles_full + tail * sp.splits;
-  return hipLaunchKernel(reinterpret_cast<const void*>(&sgemm_tile_kernel<Cfg, VEC>),
-                         dim3(static_cast<unsigned>(grid)), dim3(Cfg::NT), args, 0, stream);
-}
-
-template <class Cfg, bool VEC>
-const void* kernel_symbol() {
-  return reinterpret_cast<const void*>(&sgemm_tile_kernel<Cfg, VEC>);
+  return hipLaunchKernel(kernel_symbol<Cfg, VEC>(), dim3(static_cast<unsigned>(grid)),
+                         dim3(Cfg::NT), args, 0, stream);
 }
 
 }  // namespace fp32gemm

@@ -65,8 +65,35 @@ enum Opt : int {
   // reads four k of A per 128-bit LDS read.  The scalar variant of such a
   // tuple keeps the register-staged As[k][m] path.
   kOptDirectLds = 16,
-  kOptAll = 31,
+  // Direct-LDS option only: a two-bit field giving the LDS stages of the ring,
+  // 2 + its value (2, 3 or 4).  With S stages the loads of slice kt+S-1 are
+  // issued while slice kt is multiplied, so each slice's loads have S-1
+  // slices of compute to land in; the wait before each barrier leaves the
+  // S-2 newer slices in flight.
+  kOptStagesShift = 5,
+  kOptStagesMask = 3 << kOptStagesShift,
+  // Residency request (the tuner's occupancy axis): a two-bit field b; b > 0
+  // asks the compiler to keep b+1 workgroups resident per CU, i.e. to fit
+  // its registers to ceil((b+1) * NT / 256) waves per SIMD -- the role the
+  // pages give the second launch-bounds argument.
+  kOptOccShift = 7,
+  kOptOccMask = 3 << kOptOccShift,
+  kOptAll = 511,
 };
+
+constexpr int stages_of(const Tile& t) { return 2 + ((t.opt & kOptStagesMask) >> kOptStagesShift); }
+
+// Workgroups per CU the tuple asks for (0 = no request), and the waves per
+// SIMD that implies (1 = the compiler's default).
+constexpr int min_blocks_of(const Tile& t) {
+  return (t.opt & kOptOccMask) ? 1 + ((t.opt & kOptOccMask) >> kOptOccShift) : 0;
+}
+constexpr int waves_per_eu_of(const Tile& t) {
+  return min_blocks_of(t) ? (min_blocks_of(t) * t.NT + 255) / 256 : 1;
+}
+
+// Direct-LDS instructions per wave and slice (A plus B).
+constexpr int dma_ops_per_slice(const Tile& t) { return (t.BM * t.BK + t.BK * t.BN) / (4 * t.NT); }
 
 // Machine limits the checker enforces.
 struct Target {
@@ -109,9 +136,11 @@ enum Reason : int {
   kSwizzleRange = 16,       // swizzle needs BM, BN multiples of swz, BK <= swz, BK/4 a power of 2
   kRegisterEstimate = 17,   // estimated registers over the per-lane budget
   kNoMfmaOnTarget = 18,
-  kBadOptions = 19,         // unknown option bits, pipelining without an even k-step count, or
+  kBadOptions = 19,         // unknown option bits, pipelining without an even k-step count,
                             // direct-LDS staging on another path, with pipelining, or without
-                            // BK in {8, 16, 32, 64}
+                            // BK in {8, 16, 32, 64}, or a stage ring without direct-LDS staging,
+                            // of 5 stages, or with more loads in flight than vmcnt counts, or a
+                            // residency request beyond 8 waves per SIMD or the CU's LDS
   kNumReasons = 20,
 };
 
@@ -134,7 +163,9 @@ constexpr int lds_floats_per_stage(const Tile& t) {
 }
 
 constexpr int lds_bytes(const Tile& t, const Target& m) {
-  return m.lds_buffers * lds_floats_per_stage(t) * 4;
+  const int buffers = (t.opt & kOptDirectLds) && stages_of(t) > m.lds_buffers ? stages_of(t)
+                                                                               : m.lds_buffers;
+  return buffers * lds_floats_per_stage(t) * 4;
 }
 
 // Registers that hold one staged tile between its global load and its LDS
@@ -221,6 +252,11 @@ constexpr int check_tile(const Tile& t, const Target& m) {
       (t.path != kPathMfma32 || (t.opt & kOptPipelined) ||
        (t.BK != 8 && t.BK != 16 && t.BK != 32 && t.BK != 64)))
     return kBadOptions;
+  // The stage ring belongs to the direct-LDS loop; at most 4 stages, and the
+  // loads left in flight at each wait fit the 6-bit vmcnt counter.
+  if ((t.opt & kOptStagesMask) != 0 &&
+      (!(t.opt & kOptDirectLds) || stages_of(t) > 4 || (stages_of(t) - 2) * dma_ops_per_slice(t) > 63))
+    return kBadOptions;
 
   if (m.gfx950_rules) {
     // The As/Bs XOR swizzle flips bits below swz, in steps of at least 4
@@ -233,6 +269,11 @@ constexpr int check_tile(const Tile& t, const Target& m) {
   }
 
   if (lds_bytes(t, m) > m.lds_bytes) return kLdsOverflow;
+  // A residency request must be satisfiable: its waves fit a SIMD (8) and its
+  // workgroups' LDS fits the CU.
+  if (min_blocks_of(t) > 0 &&
+      (waves_per_eu_of(t) > 8 || min_blocks_of(t) * lds_bytes(t, m) > m.lds_bytes))
+    return kBadOptions;
   const int acc_limit = (t.path == kPathValu) ? (m.max_acc < 128 ? m.max_acc : 128) : m.max_acc;
   if (acc_per_lane(t, m.wave) > acc_limit) return kAccOverflow;
 

@@ -163,7 +163,7 @@ def test_option_guard():
     # Pipelining is an MFMA-loop option and needs an even number of k-steps.
     assert fg.check_tuple((128, 64, 16, 64, 64, 2, 4, 4, 128, VALU, 32, 1)) == 19
     assert fg.check_tuple((128, 128, 4, 128, 64, 4, 4, 1, 128, MFMA16, 0, 1)) == 19
-    assert fg.check_tuple((128, 128, 16, 64, 64, 2, 16, 1, 256, MFMA32, 32, 32)) == 19
+    assert fg.check_tuple((128, 128, 16, 64, 64, 2, 16, 1, 256, MFMA32, 32, 512)) == 19  # unknown bit
     assert fg.check_tuple((128, 128, 16, 64, 64, 2, 16, 1, 256, MFMA32, 32, 3)) == 0
     # Direct-LDS staging: MFMA 32x32x2 only, not with the pipelined loop, and
     # BK a power of two from 8 to 64.
@@ -172,6 +172,33 @@ def test_option_guard():
     assert fg.check_tuple((128, 128, 16, 64, 64, 4, 4, 1, 256, MFMA16, 32, 16)) == 19
     assert fg.check_tuple((128, 64, 16, 64, 64, 2, 4, 4, 128, VALU, 32, 16)) == 19
     assert fg.check_tuple((96, 64, 24, 32, 64, 2, 16, 1, 192, MFMA32, 0, 16)) == 19
+    # Stage rings (opt field 32 = 3 stages, 64 = 4): direct-LDS only, at most 4
+    # stages, and the LDS budget counts every stage.
+    assert fg.check_tuple((128, 128, 16, 64, 64, 2, 16, 1, 256, MFMA32, 32, 16 | 64)) == 0
+    assert fg.check_tuple((128, 128, 16, 64, 64, 2, 16, 1, 256, MFMA32, 32, 64)) == 19
+    assert fg.check_tuple((128, 128, 16, 64, 64, 2, 16, 1, 256, MFMA32, 32, 16 | 96)) == 19
+    assert fg.check_tuple((256, 256, 32, 64, 128, 4, 16, 1, 512, MFMA32, 32, 16)) == 0
+    assert fg.check_tuple((256, 256, 32, 64, 128, 4, 16, 1, 512, MFMA32, 32, 16 | 32)) == 13
+    assert fg.check_tuple((256, 256, 16, 64, 128, 4, 16, 1, 512, MFMA32, 32, 16 | 64)) == 0
+    # Residency requests (opt field 128 * b: b + 1 workgroups per CU) must fit
+    # 8 waves per SIMD and the CU's LDS.
+    assert fg.check_tuple((128, 128, 16, 32, 64, 2, 16, 1, 512, MFMA32, 32, 16 | 3 << 7)) == 0
+    assert fg.check_tuple((128, 128, 32, 32, 32, 1, 16, 1, 1024, MFMA32, 32, 1 << 7)) == 0
+    assert fg.check_tuple((128, 128, 32, 32, 32, 1, 16, 1, 1024, MFMA32, 32, 2 << 7)) == 19
+    assert fg.check_tuple((256, 256, 32, 64, 128, 4, 16, 1, 512, MFMA32, 32, 16 | 1 << 7)) == 19
+    assert fg.check_tuple((128, 64, 16, 64, 64, 2, 4, 4, 128, VALU, 32, 3 << 7)) == 0
+
+
+def test_residency_request_fields():
+    # The config table reports the request through the tuple's opt field;
+    # the hinted kernels exist for both variants.
+    hinted = [c for c in fg.configs() if c["opt"] & (3 << 7)]
+    assert hinted
+    for c in hinted:
+        assert c["resources_vec"] is not None and c["resources_scalar"] is not None
+        b = (c["opt"] >> 7) & 3
+        waves = -(-(b + 1) * c["NT"] // 256)
+        assert waves <= 8 and (b + 1) * c["lds_bytes"] <= 160 * 1024
     assert fg.check_tuple((96, 64, 24, 32, 64, 2, 16, 1, 192, MFMA32, 0, 0)) == 0
 
 
