@@ -13,8 +13,11 @@ CUS = 256
 CLOCK_HZ = 2.4e9
 FP32_FLOP_PER_CLK_PER_CU = 256          # MFMA fp32, or VALU with packed FMA
 PEAK_FP32_TFLOPS = CUS * CLOCK_HZ * FP32_FLOP_PER_CLK_PER_CU / 1e12   # 157.3 (matrix and vector)
-# Without packed-FP32 instructions a lane retires one FMA per cycle: half the
-# published vector peak (a register-only probe measures 75.8 TFLOP/s).
+# Without packed-FP32 instructions one VALU FMA instruction covers one FMA per
+# lane: nominally half the published vector peak.  (Register-only probes
+# measure the three-operand v_fma_f32 at about 75 TFLOP/s and the two-operand
+# v_fmac_f32 at 122.7 TFLOP/s, so the issue rate, not this nominal half, is
+# what bounds the VALU path.)
 PEAK_FP32_VALU_UNPACKED_TFLOPS = PEAK_FP32_TFLOPS / 2                  # 78.6
 PEAK_HBM_GBS = 8000.0
 
