@@ -113,6 +113,14 @@ def candidates():
                  (128, 128, 32, 32, 64, 2, 16, 1, 512, MFMA32, 32),
                  (128, 128, 32, 64, 64, 2, 16, 1, 256, MFMA32, 32)]:
         out += [base + (20,), base + (24,), base + (26,)]
+    # Sixteen waves per workgroup (four per SIMD), direct-to-LDS staging.
+    for BM, BN, WM, WN in [(256, 256, 64, 64), (256, 256, 128, 32), (256, 256, 32, 128),
+                           (256, 128, 64, 32), (128, 256, 32, 64), (128, 128, 32, 32)]:
+        for BK in (16, 32):
+            base = (BM, BN, BK, WM, WN, WN // 32, 16, 1, 1024, MFMA32, 32)
+            out += [base + (16,), base + (18,)]
+            if BK == 16:
+                out.append(base + (18 | 32,))
     # Direct-LDS stage rings of 3 and 4 stages (opt field 32 / 64).
     for base in [(256, 256, 16, 128, 64, 2, 16, 1, 512, MFMA32, 32),
                  (256, 256, 16, 64, 128, 4, 16, 1, 512, MFMA32, 32),

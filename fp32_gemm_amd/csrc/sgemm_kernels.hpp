@@ -161,64 +161,110 @@ __device__ __forceinline__ void stage_store(float* stage, int t, const Staged<Cf
 // a __shared__ array is an address-space cast.
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// Per-lane part of each of this wave's direct-LDS instructions that does not
-// change from slice to slice: the byte offset from the slice origin
-// (A[row0][k0] or B[k0][col0]; kMaskedOffset for rows of A past M and columns
-// of B past N), and the in-slice k the lane's float4 starts at, which decides
-// whether it lies inside K on a given slice.
-template <class Cfg>
+// Direct-LDS slices run partial-first: with nk = ceil(K / BK) slices and
+// r = K - (nk - 1) * BK (1 <= r <= BK; r = 0 when K = 0), slice 0 covers
+// k in [0, r) and slice s >= 1 covers [r + (s - 1) * BK, r + s * BK).  Only
+// slice 0 needs a mask along K (in the prologue); every slice the loop
+// loads is whole, or lies past K entirely and gets an empty resource.
+__device__ __forceinline__ int tail_width(const KernelArgs& p, int BK) {
+  return p.nk > 0 ? p.K - (p.nk - 1) * BK : 0;
+}
+__device__ __forceinline__ int slice_k0(int kt, int r, int BK) {
+  return kt == 0 ? 0 : r + (kt - 1) * BK;
+}
+
+// Per-lane byte offsets of this wave's direct-LDS instructions from the slice
+// origin (A[row0][k0], B[k0][col0]); they do not change from slice to slice.
+// Rows of A past M need no mask: they lie past the end of the slice's buffer
+// resource (lda >= K), so they load as zero without being read.  Columns of B
+// past N would fall inside the resource (the next row's elements or ldb
+// padding), so their offsets are masked here, once.
+template <class Cfg, bool VEC>
 struct DmaLanes {
   static constexpr Geom g = make_geom(Cfg::tile);
-  int a_off[dma_ops_a(g)], a_k[dma_ops_a(g)];
-  int b_off[dma_ops_b(g)], b_k[dma_ops_b(g)];
+  static constexpr int FPL = VEC ? 4 : 1;
+  int a_off[dma_ops_a(g, FPL)];
+  int b_off[dma_ops_b(g, FPL)];
 };
 
-template <class Cfg>
-__device__ __forceinline__ void dma_setup(const KernelArgs& p, int row0, int col0, int wave,
-                                          int lane, DmaLanes<Cfg>& d) {
+template <class Cfg, bool VEC>
+__device__ __forceinline__ void dma_setup(const KernelArgs& p, int col0, int wave, int lane,
+                                          DmaLanes<Cfg, VEC>& d) {
   constexpr Geom g = make_geom(Cfg::tile);
+  constexpr int FPL = DmaLanes<Cfg, VEC>::FPL;
   const int lda = static_cast<int>(p.lda), ldb = static_cast<int>(p.ldb);
-  const int rows = p.M - row0, cols = p.N - col0;
+  const int cols = p.N - col0;
 #pragma unroll
-  for (int j = 0; j < dma_ops_a(g); ++j) {
-    const MK s = dma_a_src(g, dma_op(g, wave, j), lane);
-    d.a_off[j] = s.m < rows ? (s.m * lda + 4 * s.kq) * 4 : kMaskedOffset;
-    d.a_k[j] = 4 * s.kq;
+  for (int j = 0; j < dma_ops_a(g, FPL); ++j) {
+    const MK s = dma_a_src(g, dma_op(g, wave, j), lane, FPL);
+    d.a_off[j] = (s.m * lda + s.k) * 4;
   }
 #pragma unroll
-  for (int j = 0; j < dma_ops_b(g); ++j) {
-    const KN s = dma_b_src(g, dma_op(g, wave, j), lane);
+  for (int j = 0; j < dma_ops_b(g, FPL); ++j) {
+    const KN s = dma_b_src(g, dma_op(g, wave, j), lane, FPL);
+    // In the float4 variant N % 4 == 0: a float4 is wholly inside or outside.
     d.b_off[j] = s.n < cols ? (s.k * ldb + s.n) * 4 : kMaskedOffset;
-    d.b_k[j] = s.k;
   }
 }
 
-// Issue the direct-LDS loads of the slice starting at k0 into `stage`.  The
-// float4 variant's alignment guarantees (K % 4 == 0) keep every float4 wholly
-// inside or outside K.  Completion is waited for with vmcnt before the barrier
+template <bool VEC>
+__device__ __forceinline__ void dma_load(__amdgpu_buffer_rsrc_t r, float* dst, int off) {
+  if constexpr (VEC)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(dst), 16, off, 0, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(dst), 4, off, 0, 0, 0);
+}
+
+// Issue the direct-LDS loads of the whole slice starting at k0 into `stage`
+// (or of nothing, when k0 >= K: the resources are then empty and every load
+// writes zeros).  Completion is waited for with vmcnt before the barrier
 // that publishes the stage.
-template <class Cfg>
-__device__ __forceinline__ void dma_slice(const KernelArgs& p, const DmaLanes<Cfg>& d,
+template <class Cfg, bool VEC>
+__device__ __forceinline__ void dma_slice(const KernelArgs& p, const DmaLanes<Cfg, VEC>& d,
                                           float* stage, int row0, int col0, int k0, int wave) {
   constexpr Geom g = make_geom(Cfg::tile);
+  constexpr int FPL = DmaLanes<Cfg, VEC>::FPL;
   const int kr = p.K - k0;
   const int rows = min(g.BM, p.M - row0);
   const auto ra = make_rsrc(p.A + static_cast<long long>(row0) * p.lda + k0,
-                            (static_cast<long long>(rows - 1) * p.lda + kr) * 4);
+                            kr > 0 ? (static_cast<long long>(rows - 1) * p.lda + kr) * 4 : 0);
 #pragma unroll
-  for (int j = 0; j < dma_ops_a(g); ++j) {
-    float* dst = stage + dma_op(g, wave, j) * 256;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(dst), 16,
-                                             d.a_k[j] < kr ? d.a_off[j] : kMaskedOffset, 0, 0, 0);
-  }
+  for (int j = 0; j < dma_ops_a(g, FPL); ++j)
+    dma_load<VEC>(ra, stage + dma_op(g, wave, j) * 64 * FPL, d.a_off[j]);
   const int krows = min(g.BK, kr);
   const auto rb = make_rsrc(p.B + static_cast<long long>(k0) * p.ldb + col0,
-                            (static_cast<long long>(krows - 1) * p.ldb + (p.N - col0)) * 4);
+                            kr > 0 ? (static_cast<long long>(krows - 1) * p.ldb + (p.N - col0)) * 4 : 0);
 #pragma unroll
-  for (int j = 0; j < dma_ops_b(g); ++j) {
-    float* dst = stage + g.BM * g.BK + dma_op(g, wave, j) * 256;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(dst), 16,
-                                             d.b_k[j] < kr ? d.b_off[j] : kMaskedOffset, 0, 0, 0);
+  for (int j = 0; j < dma_ops_b(g, FPL); ++j)
+    dma_load<VEC>(rb, stage + g.BM * g.BK + dma_op(g, wave, j) * 64 * FPL, d.b_off[j]);
+}
+
+// Slice 0 (k in [0, r)): the same loads with elements at k >= r masked to
+// zero in both operands (so nothing past K, even a non-finite value, meets a
+// valid term).  In the float4 variant r % 4 == 0, so a float4 is wholly
+// inside or outside.
+template <class Cfg, bool VEC>
+__device__ __forceinline__ void dma_first_slice(const KernelArgs& p, float* stage, int row0,
+                                                int col0, int r, int wave, int lane) {
+  constexpr Geom g = make_geom(Cfg::tile);
+  constexpr int FPL = VEC ? 4 : 1;
+  const int lda = static_cast<int>(p.lda), ldb = static_cast<int>(p.ldb);
+  const int rows = min(g.BM, p.M - row0);
+  const auto ra = make_rsrc(p.A + static_cast<long long>(row0) * p.lda,
+                            r > 0 ? (static_cast<long long>(rows - 1) * p.lda + r) * 4 : 0);
+#pragma unroll
+  for (int j = 0; j < dma_ops_a(g, FPL); ++j) {
+    const MK s = dma_a_src(g, dma_op(g, wave, j), lane, FPL);
+    dma_load<VEC>(ra, stage + dma_op(g, wave, j) * 64 * FPL,
+                  s.k < r ? (s.m * lda + s.k) * 4 : kMaskedOffset);
+  }
+  const auto rb = make_rsrc(p.B + col0,
+                            r > 0 ? (static_cast<long long>(r - 1) * p.ldb + (p.N - col0)) * 4 : 0);
+#pragma unroll
+  for (int j = 0; j < dma_ops_b(g, FPL); ++j) {
+    const KN s = dma_b_src(g, dma_op(g, wave, j), lane, FPL);
+    dma_load<VEC>(rb, stage + g.BM * g.BK + dma_op(g, wave, j) * 64 * FPL,
+                  s.k < r && s.n < p.N - col0 ? (s.k * ldb + s.n) * 4 : kMaskedOffset);
   }
 }
 
@@ -587,7 +633,7 @@ template <class Cfg, bool VEC>
 __device__ __forceinline__ void tile_body(const KernelArgs& p) {
   constexpr Geom g = make_geom(Cfg::tile);
   static_assert(tile_legal(Cfg::tile), "illegal tile tuple instantiated");
-  constexpr bool kDirect = VEC && (Cfg::OPT & kOptDirectLds) != 0;
+  constexpr bool kDirect = (Cfg::OPT & kOptDirectLds) != 0;
   constexpr int kStages = kDirect ? stages_of(Cfg::tile) : 2;
   __shared__ __attribute__((aligned(16))) float lds[kStages * g.STAGE];
 
@@ -627,20 +673,25 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
     // waits until its loads of slice kt+1 have landed (the S-2 newer slices'
     // loads may stay in flight); the barrier then publishes that stage to
     // every wave and also guarantees that the stage the next iteration loads
-    // into (read in this iteration) is no longer read by anyone.  Loads past
-    // the end of K are masked (they write zeros into stages no one reads
-    // again); past a segment's end they read the next segment's slices.
+    // into (read in this iteration) is no longer read by anyone.  Slices
+    // past K load nothing (zeros); past a segment's end they load the next
+    // segment's slices, which no one reads.
     constexpr int S = kStages;
-    constexpr int kInFlight = (S - 2) * dma_ops_per_slice(Cfg::tile);
-    DmaLanes<Cfg> d;
-    dma_setup<Cfg>(p, row0, col0, wave, lane, d);
+    constexpr int kInFlight = (S - 2) * dma_ops_per_slice(Cfg::tile, VEC ? 4 : 1);
+    const int r = tail_width(p, g.BK);
+    DmaLanes<Cfg, VEC> d;
+    dma_setup<Cfg, VEC>(p, col0, wave, lane, d);
 #pragma unroll
-    for (int i = 0; i < S - 1; ++i)
-      dma_slice<Cfg>(p, d, lds + i * g.STAGE, row0, col0, (kt0 + i) * g.BK, wave);
+    for (int i = 0; i < S - 1; ++i) {
+      if (i == 0 && kt0 == 0)
+        dma_first_slice<Cfg, VEC>(p, lds, row0, col0, r, wave, lane);
+      else
+        dma_slice<Cfg, VEC>(p, d, lds + i * g.STAGE, row0, col0, slice_k0(kt0 + i, r, g.BK), wave);
+    }
     ring_barrier<kInFlight>();
     int cur = 0, nxt = S - 1;
     for (int kt = kt0; kt < kt1; ++kt) {
-      dma_slice<Cfg>(p, d, lds + nxt * g.STAGE, row0, col0, (kt + S - 1) * g.BK, wave);
+      dma_slice<Cfg, VEC>(p, d, lds + nxt * g.STAGE, row0, col0, slice_k0(kt + S - 1, r, g.BK), wave);
       if constexpr (!(Cfg::OPT & kOptFloatLoads)) __builtin_amdgcn_sched_barrier(0);
       inner_product_dma<Cfg>(lds + cur * g.STAGE, wr0, wc0, lane, acc);
       ring_barrier<kInFlight>();

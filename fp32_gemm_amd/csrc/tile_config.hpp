@@ -59,11 +59,11 @@ enum Opt : int {
   // of C by beta.  Those tiles' sums are therefore not bitwise reproducible
   // from run to run (they stay within the parity bound).
   kOptSplitK = 8,
-  // MFMA 32x32x2, float4 variant: global -> LDS with buffer loads that write
-  // LDS directly (no register round-trip, no ds_write), into an As[m][k]
-  // layout whose 16-byte chunks are XOR-swizzled by row; the inner product
-  // reads four k of A per 128-bit LDS read.  The scalar variant of such a
-  // tuple keeps the register-staged As[k][m] path.
+  // MFMA 32x32x2: global -> LDS with buffer loads that write LDS directly (no
+  // register round-trip, no ds_write; 16-byte loads in the float4 variant,
+  // 4-byte loads in the scalar variant), into an As[m][k] layout whose
+  // 16-byte chunks are XOR-swizzled by row; the inner product reads four k of
+  // A per 128-bit LDS read.
   kOptDirectLds = 16,
   // Direct-LDS option only: a two-bit field giving the LDS stages of the ring,
   // 2 + its value (2, 3 or 4).  With S stages the loads of slice kt+S-1 are
@@ -92,8 +92,11 @@ constexpr int waves_per_eu_of(const Tile& t) {
   return min_blocks_of(t) ? (min_blocks_of(t) * t.NT + 255) / 256 : 1;
 }
 
-// Direct-LDS instructions per wave and slice (A plus B).
-constexpr int dma_ops_per_slice(const Tile& t) { return (t.BM * t.BK + t.BK * t.BN) / (4 * t.NT); }
+// Direct-LDS instructions per wave and slice (A plus B) for fpl floats per
+// lane (4: float4 variant, 1: scalar variant).
+constexpr int dma_ops_per_slice(const Tile& t, int fpl) {
+  return (t.BM * t.BK + t.BK * t.BN) / (fpl * t.NT);
+}
 
 // Machine limits the checker enforces.
 struct Target {
@@ -134,7 +137,8 @@ enum Reason : int {
   kAccOverflow = 14,        // accumulators per lane over the limit
   kMfmaShape = 15,          // MFMA sub-tile / lane tile / k-step mismatch
   kSwizzleRange = 16,       // swizzle needs BM, BN multiples of swz, BK <= swz, BK/4 a power of 2
-  kRegisterEstimate = 17,   // estimated registers over the per-lane budget
+  kRegisterEstimate = 17,   // estimated registers over the per-lane budget (which shrinks
+                            // when one workgroup puts several waves on each SIMD)
   kNoMfmaOnTarget = 18,
   kBadOptions = 19,         // unknown option bits, pipelining without an even k-step count,
                             // direct-LDS staging on another path, with pipelining, or without
@@ -255,7 +259,7 @@ constexpr int check_tile(const Tile& t, const Target& m) {
   // The stage ring belongs to the direct-LDS loop; at most 4 stages, and the
   // loads left in flight at each wait fit the 6-bit vmcnt counter.
   if ((t.opt & kOptStagesMask) != 0 &&
-      (!(t.opt & kOptDirectLds) || stages_of(t) > 4 || (stages_of(t) - 2) * dma_ops_per_slice(t) > 63))
+      (!(t.opt & kOptDirectLds) || stages_of(t) > 4 || (stages_of(t) - 2) * dma_ops_per_slice(t, 1) > 63))
     return kBadOptions;
 
   if (m.gfx950_rules) {
@@ -278,12 +282,16 @@ constexpr int check_tile(const Tile& t, const Target& m) {
   if (acc_per_lane(t, m.wave) > acc_limit) return kAccOverflow;
 
   if (m.gfx950_rules) {
+    // One workgroup puts ceil(NT / 256) waves on each of a CU's 4 SIMDs, which
+    // share the SIMD's 512 registers per lane.
     const int est = vgpr_estimate(t, m.wave);
+    const int per_simd = (t.NT / m.wave + 3) / 4;
+    const int budget = m.max_vgpr / per_simd;
     if (t.path == kPathValu) {
-      if (est > m.max_arch_vgpr) return kRegisterEstimate;
+      if (est > m.max_arch_vgpr || est > budget) return kRegisterEstimate;
     } else {
-      if (est > m.max_arch_vgpr || est + acc_per_lane(t, m.wave) > m.max_vgpr)
-        return kRegisterEstimate;
+      const int total = est + acc_per_lane(t, m.wave);
+      if (est > m.max_arch_vgpr || total > m.max_vgpr || total > budget) return kRegisterEstimate;
     }
   }
   return kLegal;

@@ -97,18 +97,21 @@ FG_HD constexpr int bs_index(const Geom& g, int k, int n) {
   return g.BK * g.SA + k * g.SB + (n ^ swz_b(g, k));
 }
 
-// ---- direct-LDS staging (MFMA 32x32x2, float4 variant) --------------------
-// A buffer load that writes LDS places lane l's 16 bytes at the instruction's
-// LDS base + 16*l: each wave instruction fills 256 consecutive floats, and
-// only the global address is chosen per lane.  A float4 of A is four k of one
-// row, so this layout keeps As as [m][k]: row m holds KQ = BK/4 chunks, chunk
-// kq stored at chunk position kq ^ dma_sw(m).  The fragment read is 128 bits
-// (four k of one row per lane); the LDS serves such a read in phases of
-// 8 lanes (32 banks) or 16 lanes (64 banks), and the swizzle makes the rows a
-// phase touches fall on distinct bank groups under both models: with r32 and
-// r64 rows sharing one 128-byte or 256-byte bank sweep, it combines the row
-// index divided by each (a Gray-code-like XOR, so one term's repeats are the
-// other's distinct values).  Bs stays [k][n] with the swz_b chunk swizzle.
+// ---- direct-LDS staging (MFMA 32x32x2) ----------------------------------
+// A buffer load that writes LDS places lane l's data at the instruction's LDS
+// base + (bytes per lane)*l: each wave instruction fills 64*FPL consecutive
+// floats, FPL = 4 for the float4 variant (16-byte loads) and 1 for the scalar
+// variant (4-byte loads), and only the global source is chosen per lane.  A
+// float4 of A is four k of one row, so this layout keeps As as [m][k]: row m
+// holds KQ = BK/4 16-byte chunks, chunk kq stored at chunk position
+// kq ^ dma_sw(m).  The fragment read is 128 bits (four k of one row per
+// lane); the LDS serves such a read in phases of 8 lanes (32 banks) or 16
+// lanes (64 banks), and the swizzle makes the rows a phase touches fall on
+// distinct bank groups under both models: with r32 and r64 rows sharing one
+// 128-byte or 256-byte bank sweep, it combines the row index divided by each
+// (a Gray-code-like XOR, so one term's repeats are the other's distinct
+// values).  It repeats every 16 rows.  Bs stays [k][n] with the swz_b chunk
+// swizzle.
 FG_HD constexpr int dma_sw(const Geom& g, int m) {
   const int r32 = g.KQ >= 8 ? 1 : 8 / g.KQ;
   const int r64 = g.KQ >= 16 ? 1 : 16 / g.KQ;
@@ -118,24 +121,24 @@ FG_HD constexpr int dma_sw(const Geom& g, int m) {
 FG_HD constexpr int dma_as_index(const Geom& g, int m, int k) {
   return m * g.BK + 4 * ((k >> 2) ^ dma_sw(g, m)) + (k & 3);
 }
-// Direct-LDS instructions per wave and slice (A, B), and the wave-wide
-// instruction index of a wave's j-th one.
-FG_HD constexpr int dma_ops_a(const Geom& g) { return g.BM * g.BK / (4 * g.NT); }
-FG_HD constexpr int dma_ops_b(const Geom& g) { return g.BK * g.BN / (4 * g.NT); }
+// Direct-LDS instructions per wave and slice (A, B) for FPL floats per lane,
+// and the workgroup-wide instruction index of a wave's j-th one.
+FG_HD constexpr int dma_ops_a(const Geom& g, int fpl) { return g.BM * g.BK / (fpl * g.NT); }
+FG_HD constexpr int dma_ops_b(const Geom& g, int fpl) { return g.BK * g.BN / (fpl * g.NT); }
 FG_HD constexpr int dma_op(const Geom& g, int w, int j) { return j * (g.NT / 64) + w; }
-// Source of lane l in A instruction i: row m and chunk kq of the A slice (its
-// LDS position is float i*256 + 4*l of the A stage).
-struct MK { int m, kq; };
-FG_HD constexpr MK dma_a_src(const Geom& g, int i, int l) {
-  const int f = i * 256 + 4 * l;
-  const int m = f / g.BK;
-  return MK{m, ((f % g.BK) >> 2) ^ dma_sw(g, m)};
+// Source of lane l in A instruction i: row m and first column k of the FPL
+// elements it fetches (they land at float i*64*FPL + FPL*l of the A stage).
+struct MK { int m, k; };
+FG_HD constexpr MK dma_a_src(const Geom& g, int i, int l, int fpl) {
+  const int f = (i * 64 + l) * fpl;
+  const int m = f / g.BK, kk = f % g.BK;
+  return MK{m, (((kk >> 2) ^ dma_sw(g, m)) << 2) | (kk & 3)};
 }
-// Source of lane l in B instruction i: k-row and first column of the float4
-// (LDS float BK*BM + i*256 + 4*l of the stage).
+// Source of lane l in B instruction i: k-row and first column (LDS float
+// BK*BM + i*64*FPL + FPL*l of the stage).
 struct KN { int k, n; };
-FG_HD constexpr KN dma_b_src(const Geom& g, int i, int l) {
-  const int f = i * 256 + 4 * l;
+FG_HD constexpr KN dma_b_src(const Geom& g, int i, int l, int fpl) {
+  const int f = (i * 64 + l) * fpl;
   const int k = f / g.BN;
   return KN{k, (f % g.BN) ^ swz_b(g, k)};
 }

@@ -111,7 +111,9 @@ typedef struct sgemm_config_t {
   int32_t opt; /* schedule options: bit 0 pipelined MFMA loop, bit 1 XCD-aware tile order,
                   bit 2 unpinned global loads, bit 3 split-K for a partly filled last wave
                   (those tiles accumulate with fp32 atomics: not bitwise reproducible),
-                  bit 4 direct global-to-LDS loads in the float4 variant (MFMA 32x32x2) */
+                  bit 4 direct global-to-LDS loads (MFMA 32x32x2; 16-byte loads in the
+                  float4 variant, 4-byte loads in the scalar one), bits 5-6 with bit 4:
+                  LDS stages - 2, bits 7-8: workgroups per CU requested - 1 (0 = none) */
   int32_t WMITER, WSUBM, WSUBN;
   int32_t acc_per_lane;
   int32_t lds_bytes;     /* both LDS stages */
@@ -186,8 +188,8 @@ int sgemm_check_tuple(const int32_t tuple[12], int32_t target);
  * accumulator sees every k of a slice exactly once.  Also reports the LDS
  * bank-conflict degree of each access class under a banks-wide model
  * (32 or 64 four-byte banks).  For tuples with the direct-LDS option it
- * also checks that layout (checks 6-8: the direct loads fill each stage
- * exactly once where the layout expects each float4, and the 8-k-group
+ * also checks that layout for both load widths (checks 6-8: the direct
+ * loads fill each stage exactly once where the layout expects each element, and the 8-k-group
  * fragment reads feed every accumulator each k once).  Returns 0 when all
  * checks pass, the checker's reason code if the tuple is illegal, or 100+n
  * for failed check n. */

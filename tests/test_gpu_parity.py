@@ -176,6 +176,41 @@ def test_split_configs_random_inputs_within_tolerance(fg, dev, orc):
         check_close(cv.result(), r64b, K, A, B, f"split cfg {c['id']} beta=0")
 
 
+@pytest.mark.parametrize("variant", ["vec", "scalar"])
+def test_direct_lds_configs_short_and_ragged_K(fg, dev, orc, variant):
+    # Direct-to-LDS configs run their K slices partial-first: slice 0 holds the
+    # K % BK remainder (masked in both operands) and every later slice is
+    # whole.  K = 0 (no slice), K below one slice, a one-column tail and a
+    # tail one past a whole slice, on ragged M and N, for both load widths.
+    cfgs = [c for c in fg.configs() if c["opt"] & 16]
+    N = 92 if variant == "vec" else 91
+    pad = 4 if variant == "vec" else 5
+    for K in ((0, 4, 36, 64) if variant == "vec" else (0, 1, 33, 65)):
+        log(f"[direct-lds] {variant} 70x{N}x{K}: {len(cfgs)} configs")
+        if K == 0:
+            C = inputs.make_random(70, N, 1, seed=1700)[2]
+            want = (3.0 * C.astype(np.float64)).astype(np.float32)
+            A0 = torch.empty((70, 0), dtype=torch.float32, device=dev)
+            B0 = torch.empty((0, N), dtype=torch.float32, device=dev)
+            for c in cfgs:
+                cv = Canvas(C, N + pad, 3, dev)
+                fg.sgemm_ex(A0, B0, cv.view, 0.5, 3.0, cfg_id=c["id"])
+                torch.cuda.synchronize()
+                assert cv.untouched() and np.array_equal(cv.result(), want), f"cfg {c['id']} K=0"
+            continue
+        A, B, C = inputs.make_random(70, N, K, seed=1700 + K)
+        Ai, Bi, Ci = inputs.make_small_int(70, N, K, seed=1800 + K)
+        r64 = orc.sgemm(A, B, C, 0.5, 3.0)[1]
+        i32 = orc.sgemm(Ai, Bi, Ci, 0.5, 3.0)[0]
+        for c in cfgs:
+            cv = run(fg, dev, A, B, C, 0.5, 3.0, cfg=c["id"], ldc_pad=pad)
+            assert cv.untouched(), f"cfg {c['id']} K={K}: wrote outside C"
+            check_close(cv.result(), r64, K, A, B, f"cfg {c['id']} K={K}")
+            cv = run(fg, dev, Ai, Bi, Ci, 0.5, 3.0, cfg=c["id"], ldc_pad=pad)
+            assert np.array_equal(cv.result().view(np.uint32), i32.view(np.uint32)), \
+                f"cfg {c['id']} K={K}: integer inputs not bit-exact"
+
+
 @pytest.mark.parametrize("rung", [1, 2, 3, 4])
 def test_ladder_rungs(fg, dev, orc, rung):
     """Each rung of the kernel ladder on ragged shapes: within tolerance on
