@@ -133,6 +133,32 @@ def test_every_config_both_variants(fg, dev, ragged_cases, chunk):
     log(f"[parity] worst err {worst:.3e}")
 
 
+@pytest.mark.parametrize("variant", ["vec", "scalar"])
+def test_every_config_reads_inside_K(fg, dev, orc, variant):
+    # A and B sit in NaN-filled buffers: NaN in the lda / ldb padding and in
+    # the rows after B's K rows.  A read of any element outside the logical
+    # K range would put a NaN into a stored output; the results must instead
+    # match the oracle.  (Reads past M or N could only reach outputs that are
+    # never stored; the buffer resources bound those.)
+    M, N, K, pad = (130, 100, 76, 4) if variant == "vec" else (130, 97, 75, 3)
+    A, B, C = inputs.make_random(M, N, K, seed=77 + K)
+    _, r64 = orc.sgemm(A, B, C, 0.5, 3.0)
+    Abig = torch.full((M + 8, K + pad), float("nan"), device=dev)
+    Bbig = torch.full((K + 8, N + pad), float("nan"), device=dev)
+    Abig[:M, :K] = torch.from_numpy(A).to(dev)
+    Bbig[:K, :N] = torch.from_numpy(B).to(dev)
+    cfgs = fg.configs()
+    log(f"[nan-padding] {variant} {M}x{N}x{K}: {len(cfgs)} configs")
+    for c in cfgs:
+        cv = Canvas(C, N + pad, 2, dev)
+        fg.sgemm_ex(Abig[:M, :K], Bbig[:K, :N], cv.view, 0.5, 3.0, cfg_id=c["id"])
+        torch.cuda.synchronize()
+        assert cv.untouched(), f"cfg {c['id']}: wrote outside C"
+        got = cv.result()
+        assert np.isfinite(got).all(), f"cfg {c['id']} {c['tuple']}: read outside K"
+        check_close(got, r64, K, A, B, f"cfg {c['id']} {variant}")
+
+
 def test_split_configs_with_whole_and_split_tiles(fg, dev, orc):
     """Every split-K configuration on a shape whose tiles overflow the
     resident workgroups by a small tail, so whole tiles and atomically summed
