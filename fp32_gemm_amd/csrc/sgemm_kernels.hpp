@@ -794,6 +794,7 @@ hipError_t launch_tile(const KernelArgs& a, hipStream_t stream, long long slots)
   KernelArgs k = a;
   const long long tiles_m = (a.M + Cfg::BM - 1) / Cfg::BM;
   const long long tiles_n = (a.N + Cfg::BN - 1) / Cfg::BN;
+  if (tiles_m * tiles_n > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
   k.tiles_m = static_cast<int>(tiles_m);
   k.tiles_n = static_cast<int>(tiles_n);
   k.group_m = xcd_group_rows(tiles_m, tiles_n, Cfg::BM, Cfg::BN);
@@ -811,6 +812,7 @@ hipError_t launch_tile(const KernelArgs& a, hipStream_t stream, long long slots)
     if (e != hipSuccess) return e;
   }
   const long long grid = sp.tiles_full + tail * sp.splits;
+  if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
   return hipLaunchKernel(kernel_symbol<Cfg, VEC>(), dim3(static_cast<unsigned>(grid)),
                          dim3(Cfg::NT), args, 0, stream);
 }

@@ -60,6 +60,15 @@ def test_argument_codes(args, code):
     assert plan(*args)[0] == code
 
 
+def test_tile_count_beyond_int32_is_unsupported():
+    # 2^30 x (2^21 - 1) outputs need more than 2^31 - 1 workgroups with any
+    # compiled tile; the sizes themselves are within the limits.
+    M, N = 1 << 30, (1 << 21) - 1
+    for cfg in (0, fg.num_configs() - 1):
+        assert plan(M, N, 4, 4, N, N, cfg=cfg)[0] == 5
+    assert plan(M, 64, 4, 4, 64, 64, cfg=0)[0] == 0
+
+
 def test_null_pointers():
     assert plan(4, 4, 4, 4, 4, 4, A=None)[0] == -5
     assert plan(4, 4, 4, 4, 4, 4, B=None)[0] == -7
