@@ -74,6 +74,13 @@ def candidates():
         (128, 128, 16, 128, 64, 2, 8, 4, 128),
         (256, 128, 16, 128, 64, 2, 8, 4, 256),
         (128, 128, 32, 64, 64, 2, 4, 4, 256),
+        # 8x16 and 16x8 lane patches: 0.75 LDS bytes per FMA instead of 1.
+        (128, 128, 16, 64, 128, 1, 8, 16, 128),
+        (128, 128, 8, 64, 128, 1, 8, 16, 128),
+        (128, 256, 16, 64, 128, 1, 8, 16, 256),
+        (256, 256, 16, 128, 128, 1, 8, 16, 256),
+        (128, 128, 16, 128, 64, 1, 16, 8, 128),
+        (256, 128, 16, 128, 64, 1, 16, 8, 256),
     ]:
         out.append(t + (VALU, 32, 0))
         out.append(t + (VALU, 32, 2))
