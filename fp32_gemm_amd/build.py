@@ -120,6 +120,16 @@ def candidates():
                  (128, 128, 32, 32, 64, 2, 16, 1, 512, MFMA32, 32),
                  (128, 128, 32, 64, 64, 2, 16, 1, 256, MFMA32, 32)]:
         out += [base + (20,), base + (24,), base + (26,)]
+    # Direct-LDS on smaller tiles (more workgroups per CU for mid-size shapes).
+    for BM, BN in [(128, 64), (64, 128), (64, 64)]:
+        for BK in (16, 32, 64):
+            for WM in (32, 64):
+                for WN in (32, 64):
+                    waves = (BM // WM) * (BN // WN)
+                    if WM > BM or WN > BN or waves not in (2, 4, 8):
+                        continue
+                    base = (BM, BN, BK, WM, WN, WN // 32, 16, 1, 64 * waves, MFMA32, 32)
+                    out += [base + (16,), base + (18,), base + (24,)]
     # Sixteen waves per workgroup (four per SIMD), direct-to-LDS staging.
     for BM, BN, WM, WN in [(256, 256, 64, 64), (256, 256, 128, 32), (256, 256, 32, 128),
                            (256, 128, 64, 32), (128, 256, 32, 64), (128, 128, 32, 32)]:

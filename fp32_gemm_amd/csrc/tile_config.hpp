@@ -265,10 +265,12 @@ constexpr int check_tile(const Tile& t, const Target& m) {
   if (m.gfx950_rules) {
     // The As/Bs XOR swizzle flips bits below swz, in steps of at least 4
     // words, so it needs swz-aligned rows and at most swz/4 groups of four
-    // k-rows per staged tile.
+    // k-rows per staged tile.  Direct-LDS tuples keep As as [m][k] with their
+    // own chunk swizzle; for them only the Bs part applies.
     if (t.swz != 0 && t.swz != 32 && t.swz != 64) return kSwizzleRange;
-    if (t.swz != 0 && (t.BM % t.swz != 0 || t.BN % t.swz != 0 || t.BK > t.swz ||
-                       ((t.BK / 4) & (t.BK / 4 - 1)) != 0))
+    if (t.swz != 0 && t.BN % t.swz != 0) return kSwizzleRange;
+    if (t.swz != 0 && !(t.opt & kOptDirectLds) &&
+        (t.BM % t.swz != 0 || t.BK > t.swz || ((t.BK / 4) & (t.BK / 4 - 1)) != 0))
       return kSwizzleRange;
   }
 

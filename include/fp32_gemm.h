@@ -195,9 +195,9 @@ int sgemm_check_tuple(const int32_t tuple[12], int32_t target);
  * for failed check n. */
 typedef struct sgemm_sim_report_t {
   int32_t failed_check;   /* 0 = all passed */
-  int32_t store_a_ways;   /* transposed A store, ds_write_b32 */
-  int32_t store_b_ways;   /* B store, ds_write_b128 */
-  int32_t read_a_ways;    /* fragment reads of As */
+  int32_t store_a_ways;   /* transposed A store, ds_write_b32 (register-staged layout only; */
+  int32_t store_b_ways;   /* B store, ds_write_b128            1 for direct-LDS tuples, which */
+  int32_t read_a_ways;    /* fragment reads of As              do not use that layout) */
   int32_t read_b_ways;    /* fragment reads of Bs */
   int32_t dma_read_a_ways; /* direct-LDS option: 128-bit As[m][k] reads (0 without it) */
   int32_t dma_read_b_ways; /* direct-LDS option: Bs reads (0 without it) */
