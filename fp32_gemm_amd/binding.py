@@ -235,11 +235,15 @@ def sgemm_ex(A, B, C, alpha=1.0, beta=0.0, stream=None, cfg_id=-1):
         raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, C {tuple(C.shape)}")
     if not (A.device == B.device == C.device):
         raise ValueError("A, B and C must be on the same device")
+    dev = C.device
     if stream is None:
-        stream = torch.cuda.current_stream(C.device)
+        stream = torch.cuda.current_stream(dev)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
-    with torch.cuda.device(C.device):
+    if dev.index == torch.cuda.current_device():
         rc = _lib.sgemm_ex(M, N, K, alpha, a, lda, b, ldb, beta, c, ldc, handle, cfg_id)
+    else:
+        with torch.cuda.device(dev):
+            rc = _lib.sgemm_ex(M, N, K, alpha, a, lda, b, ldb, beta, c, ldc, handle, cfg_id)
     if rc != 0:
         raise SgemmError(rc)
     return C
