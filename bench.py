@@ -26,7 +26,9 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="untimed launches first; in a fresh process the first launches after "
+                         "only ten warm-ups still run 5-10%% slower")
     ap.add_argument("--workload", default="sq4096")
     ap.add_argument("--cfg", type=int, default=-1, help="force a configuration id")
     ap.add_argument("--tile", default=None,
@@ -143,7 +145,10 @@ def main():
     Bd = torch.from_numpy(B).to(dev)
     C0 = torch.from_numpy(C).to(dev)
     total = args.warmup + args.steps
-    pool = min(total, 64)
+    # One pristine C per launch (cold in the caches, and beta * C never
+    # compounds), within an 8 GiB budget; past it buffers are reused and the
+    # timed ones are refilled after the warm-up.
+    pool = max(1, min(total, (8 << 30) // max(1, C0.numel() * 4)))
     Cs = [C0.clone() for _ in range(pool)]
     stream = torch.cuda.current_stream(dev)
     plan = fg.binding.plan(w.M, w.N, w.K, Ad.data_ptr(), w.K, Bd.data_ptr(), w.N,
@@ -155,9 +160,10 @@ def main():
 
     for i in range(args.warmup):
         step(i)
-    # Refill the buffers the timed steps will use with the pristine C.
-    for i in range(args.steps):
-        Cs[(args.warmup + i) % pool].copy_(C0)
+    if pool < total:
+        # Buffers are reused: give the timed steps pristine C again.
+        for i in range(args.steps):
+            Cs[(args.warmup + i) % pool].copy_(C0)
     torch.cuda.synchronize()
 
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
