@@ -29,7 +29,11 @@
  * stream for sgemm(), the caller's for sgemm_ex()); buffers must stay alive
  * until the stream passes the call.  Results are visible after a stream
  * synchronisation.  The entry points are thread-safe (no mutable global state
- * besides a per-device capability cache).
+ * besides per-device capability and occupancy caches).  A call may be recorded
+ * into a stream capture (HIP graph): it enqueues only kernel launches (two for
+ * a split-K configuration: a beta pre-pass and the GEMM), no memset or copy;
+ * make one uncaptured call with the same configuration on the device first, so
+ * the caches are filled outside the capture.
  *
  * Errors: validation happens before anything is enqueued and never launches.
  * A negative status -i names the i-th argument (1-based) as illegal, BLAS

@@ -435,6 +435,47 @@ def test_overlap_rejected(fg, dev):
     assert e.value.status == 3
 
 
+def test_graph_capture_replays(fg, dev, orc):
+    # sgemm_ex records into a stream capture like any launch on that stream
+    # (the split-K pre-pass is a kernel, not a memset).  Each replay, with
+    # eager work and synchronisation in between, must reproduce the eager
+    # result: bit for bit where the configuration is deterministic, within
+    # the tolerance for a split configuration (its atomics commit in any
+    # order).
+    M, N, K = 600, 520, 300
+    A, B, C = inputs.make_random(M, N, K, seed=31)
+    _, r64 = orc.sgemm(A, B, C, 0.5, 3.0)
+    Ad, Bd, C0 = to_dev(A, dev), to_dev(B, dev), to_dev(C, dev)
+    split = [c["id"] for c in fg.configs() if c["opt"] & 8 and c["opt"] & 16][0]
+    for cfg in (-1, split):
+        log(f"[graph] cfg {cfg}")
+        Ce = C0.clone()
+        fg.sgemm_ex(Ad, Bd, Ce, 0.5, 3.0, cfg_id=cfg)
+        torch.cuda.synchronize()
+        eager = Ce.cpu().numpy()
+        check_close(eager, r64, K, A, B, f"eager cfg {cfg}")
+        Cg = C0.clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fg.sgemm_ex(Ad, Bd, Cg, 0.5, 3.0, cfg_id=cfg)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fg.sgemm_ex(Ad, Bd, Cg, 0.5, 3.0, cfg_id=cfg)
+        for rep in range(4):
+            Cg.copy_(C0)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            got = Cg.cpu().numpy()
+            if cfg == split:
+                check_close(got, r64, K, A, B, f"replay {rep} cfg {cfg}")
+            else:
+                assert np.array_equal(got.view(np.uint32), eager.view(np.uint32)), f"replay {rep}"
+
+
 def test_side_stream(fg, dev, orc):
     M, N, K = 512, 512, 512
     A, B, C = inputs.make_random(M, N, K, seed=11)
