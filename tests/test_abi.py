@@ -111,6 +111,22 @@ def test_tuned_dispatch_picks_a_compiled_config():
         assert p["grid"] == -(-M // info["BM"]) * -(-N // info["BN"])
 
 
+def test_tuned_table_tuples_are_compiled():
+    # Every rule and default of the tuned table names a compiled tuple, and
+    # each tuned shape dispatches to exactly that tuple.
+    text = open(os.path.join(ROOT, "fp32_gemm_amd", "csrc", "tuned_table.inc")).read()
+    compiled = {tuple(c["tuple"]) for c in fg.configs()}
+    rules = re.findall(r"\{(\d+), (\d+), (\d+), \{([\d, ]+)\}\}", text)
+    assert rules
+    for M, N, K, tup in rules:
+        t = tuple(int(x) for x in tup.split(","))
+        assert t in compiled, t
+        code, p = plan(int(M), int(N), int(K), int(K), int(N), int(N))
+        assert code == 0 and tuple(fg.config_info(p["cfg_id"])["tuple"]) == t
+    for d in re.findall(r"Tile kDefault\w+\{([\d, ]+)\}", text):
+        assert tuple(int(x) for x in d.split(",")) in compiled
+
+
 def test_quick_return_and_no_device():
     # M == 0: nothing to do, success without a device.
     assert binding.sgemm_raw(0, 4, 4, 1.0, FAKE, 4, FAKE * 2, 4, 0.0, FAKE * 4, 4) == 0
