@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--no-context", action="store_true", help="skip timing torch.mm")
     ap.add_argument("--ladder", action="store_true",
                     help="only time the four ladder rungs on the workload (one JSON line)")
+    ap.add_argument("--oracle-timing", action="store_true",
+                    help="only time the CPU oracle on every workload (one JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -72,6 +74,46 @@ def cpu_baseline(w, A, B, C, target_s):
     return {"value": round(gflops, 3), "unit": "GFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"first {rows} of {w.M} rows of the same {w.M}x{w.N}x{w.K} product "
                       f"(fp64 accumulation, OpenMP over rows), {dt:.1f} s"}
+
+
+def oracle_timing(inputs, model, max_seconds=20.0):
+    """The oracle, as it stands, on every workload: the whole product where it
+    takes at most `max_seconds`, else the first rows scaled to that time; one
+    thread as well for the two smallest squares.  Reported only."""
+    from oracle import oracle
+    oracle.build(force=False)
+    threads = oracle.max_threads()
+    model_name = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model_name = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    out = []
+
+    def run(w, A, B, C, nthreads):
+        oracle.set_threads(nthreads)
+        rows = min(w.M, 8)
+        t0 = time.perf_counter()
+        oracle.sgemm(A[:rows], B, C[:rows], w.alpha, w.beta)
+        probe = max(time.perf_counter() - t0, 1e-4)
+        rows = int(min(w.M, max(rows, rows * max_seconds / probe)))
+        t0 = time.perf_counter()
+        oracle.sgemm(A[:rows], B, C[:rows], w.alpha, w.beta)
+        dt = time.perf_counter() - t0
+        return {"workload": w.name, "threads": nthreads, "rows": rows, "of_rows": w.M,
+                "seconds": round(dt, 4), "GFLOP/s": round(2.0 * rows * w.N * w.K / dt / 1e9, 3)}
+
+    for name, w in inputs.WORKLOADS.items():
+        A, B, C = inputs.make(w)
+        out.append(run(w, A, B, C, threads))
+        if name in ("sq256", "sq1024"):
+            out.append(run(w, A, B, C, 1))
+        print(json.dumps(out[-1]), file=sys.stderr, flush=True)
+    oracle.set_threads(threads)
+    print(json.dumps({"oracle_timing": out, "cores": threads, "cpu_model": model_name,
+                      "kind": "oracle", "note": "fp64 accumulation, OpenMP over rows; reported only"}),
+          flush=True)
 
 
 def ladder(fg, inputs, model, w, dev, args):
@@ -115,6 +157,11 @@ def main():
         print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} "
               f"(WORLD_SIZE={world}) is not supported", file=sys.stderr, flush=True)
         sys.exit(2)
+
+    if args.oracle_timing:
+        from fp32_gemm_amd import inputs, model
+        oracle_timing(inputs, model)
+        return
 
     import numpy as np
     import torch
