@@ -289,7 +289,9 @@ def main():
             torch.mm(Ad, Bd, out=Cm)
         e1.record(stream)
         torch.cuda.synchronize()
-        out["context"] = {"torch_mm_tflops": round(flops / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e12, 2),
+        mm = flops / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e12
+        out["context"] = {"torch_mm_tflops": round(mm, 2),
+                          "this_vs_torch_mm": round(achieved / mm, 3),
                           "note": "vendor BLAS timing, context only; never used for dispatch or parity"}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, A, B, C, args.cpu_seconds)
