@@ -146,7 +146,7 @@ def write_table(best_by_shape, path, defaults):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--workloads", default=",".join(inputs.WORKLOADS))
-    ap.add_argument("--out", default="gpurun_out/tune_results.jsonl")
+    ap.add_argument("--out", default="tune_results.jsonl")
     ap.add_argument("--table-out", default=None)
     ap.add_argument("--paths", default="valu,mfma32,mfma16")
     ap.add_argument("--prune-above", type=float, default=2 * 4096 ** 3 * 1.5,
