@@ -39,7 +39,7 @@ class _Config(ctypes.Structure):
 
 class _Plan(ctypes.Structure):
     _fields_ = [("cfg_id", _i32), ("vector_variant", _i32), ("grid", _i64), ("block", _i32),
-                ("tiles_full", _i32), ("splits", _i32)]
+                ("tiles_full", _i32), ("splits", _i32), ("slots", _i64)]
 
 
 class _Attr(ctypes.Structure):

@@ -137,12 +137,19 @@ typedef struct sgemm_plan_t {
   int32_t block;          /* threads per workgroup */
   int32_t tiles_full;     /* output tiles computed whole by one workgroup */
   int32_t splits;         /* K segments of each remaining tile (1 = none) */
+  int64_t slots;          /* workgroups of this kernel resident on the current device
+                             at once (compute units x occupancy); 0 without a device */
 } sgemm_plan_t;
 
 /* Validates like sgemm_ex (same status codes, no device check) and fills
- * *out.  cfg_id < 0 selects the tuned configuration.  The split decision
- * needs the device's compute-unit count; without a device it reports no
- * split. */
+ * *out.  cfg_id < 0 selects the tuned configuration: the exact-shape rule,
+ * else the nearest rule in (log M, log N, log K), which (from 2^30 FLOP up)
+ * gives way to the nearest rule with a split-K tuple when its tile would leave
+ * more than a tenth of the resident workgroup slots idle in the last wave.
+ * Split-K tiles add partial sums with atomics, so their last bits may differ
+ * from run to run (within the accuracy bound).  The split
+ * decision and that check need the device's compute units and occupancy;
+ * without a device the nearest rule and no split are reported. */
 int sgemm_plan(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
                int64_t ldb, const float* C, int64_t ldc, int32_t cfg_id, sgemm_plan_t* out);
 
