@@ -138,6 +138,41 @@ def candidates():
             out += [base + (16,), base + (18,)]
             if BK == 16:
                 out.append(base + (18 | 32,))
+    # Direct-LDS staging on MFMA 16x16x4: sixteen independent accumulator
+    # chains per wave on 64x64 wave tiles (the 32x32x2 tiles above carry four
+    # or eight), under both bank models.
+    for BM, BN, WM, WN in [(128, 128, 64, 64), (256, 128, 64, 64), (128, 256, 64, 64),
+                           (256, 256, 64, 64), (256, 256, 128, 64), (128, 128, 64, 32),
+                           (128, 128, 32, 64)]:
+        waves = (BM // WM) * (BN // WN)
+        for BK in (16, 32, 64):
+            for swz in (32, 64):
+                base = (BM, BN, BK, WM, WN, WN // 16, 4, 1, 64 * waves, MFMA16, swz)
+                out += [base + (16,), base + (18,), base + (24,), base + (26,)]
+                if BM * BN <= 128 * 128:
+                    out.append(base + (18 | 128,))
+                if BK == 16:
+                    out.append(base + (18 | 32,))
+    # Direct-LDS with the k-group pipeline (opt bit 1): the slice's last
+    # k-group multiplied across the barrier.
+    for base in [(256, 256, 32, 128, 32, 1, 16, 1, 1024, MFMA32, 32),
+                 (256, 256, 16, 128, 32, 1, 16, 1, 1024, MFMA32, 32),
+                 (256, 256, 32, 64, 64, 2, 16, 1, 1024, MFMA32, 32),
+                 (256, 256, 32, 128, 64, 2, 16, 1, 512, MFMA32, 32),
+                 (256, 256, 32, 64, 128, 4, 16, 1, 512, MFMA32, 32),
+                 (128, 128, 32, 64, 64, 2, 16, 1, 256, MFMA32, 32),
+                 (256, 256, 32, 128, 64, 4, 4, 1, 512, MFMA16, 32),
+                 (256, 256, 32, 64, 64, 4, 4, 1, 1024, MFMA16, 64),
+                 (128, 256, 16, 64, 64, 4, 4, 1, 512, MFMA16, 32),
+                 (128, 256, 32, 64, 64, 4, 4, 1, 512, MFMA16, 32),
+                 (128, 128, 16, 64, 64, 4, 4, 1, 256, MFMA16, 32),
+                 (128, 128, 32, 64, 64, 4, 4, 1, 256, MFMA16, 32),
+                 (128, 128, 64, 64, 32, 2, 4, 1, 512, MFMA16, 64)]:
+        out += [base + (17,), base + (19,), base + (25,), base + (27,)]
+        if base[0] * base[1] <= 128 * 128:
+            out.append(base + (19 | 128,))
+        if base[2] == 16:
+            out.append(base + (19 | 32,))
     # Direct-LDS stage rings of 3 and 4 stages (opt field 32 / 64).
     for base in [(256, 256, 16, 128, 64, 2, 16, 1, 512, MFMA32, 32),
                  (256, 256, 16, 64, 128, 4, 16, 1, 512, MFMA32, 32),

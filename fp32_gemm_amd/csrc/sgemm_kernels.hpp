@@ -215,28 +215,35 @@ __device__ __forceinline__ void dma_load(__amdgpu_buffer_rsrc_t r, float* dst, i
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(dst), 4, off, 0, 0, 0);
 }
 
-// Issue the direct-LDS loads of the whole slice starting at k0 into `stage`
-// (or of nothing, when k0 >= K: the resources are then empty and every load
-// writes zeros).  Completion is waited for with vmcnt before the barrier
-// that publishes the stage.
-template <class Cfg, bool VEC>
+// Issue the direct-LDS loads of the slice starting at k0 into `stage` (or of
+// nothing, when k0 >= K: the resources are then empty and every load writes
+// zeros): part PART of PARTS, the wave's A instructions followed by its B
+// instructions cut into PARTS consecutive runs.  Completion is waited for
+// with vmcnt before the barrier that publishes the stage.
+template <class Cfg, bool VEC, int PART = 0, int PARTS = 1>
 __device__ __forceinline__ void dma_slice(const KernelArgs& p, const DmaLanes<Cfg, VEC>& d,
                                           float* stage, int row0, int col0, int k0, int wave) {
   constexpr Geom g = make_geom(Cfg::tile);
   constexpr int FPL = DmaLanes<Cfg, VEC>::FPL;
+  constexpr int NA = dma_ops_a(g, FPL), NB = dma_ops_b(g, FPL);
+  constexpr int U0 = PART * (NA + NB) / PARTS, U1 = (PART + 1) * (NA + NB) / PARTS;
   const int kr = p.K - k0;
-  const int rows = min(g.BM, p.M - row0);
-  const auto ra = make_rsrc(p.A + static_cast<long long>(row0) * p.lda + k0,
-                            kr > 0 ? (static_cast<long long>(rows - 1) * p.lda + kr) * 4 : 0);
+  if constexpr (U0 < NA) {
+    const int rows = min(g.BM, p.M - row0);
+    const auto ra = make_rsrc(p.A + static_cast<long long>(row0) * p.lda + k0,
+                              kr > 0 ? (static_cast<long long>(rows - 1) * p.lda + kr) * 4 : 0);
 #pragma unroll
-  for (int j = 0; j < dma_ops_a(g, FPL); ++j)
-    dma_load<VEC>(ra, stage + dma_op(g, wave, j) * 64 * FPL, d.a_off[j]);
-  const int krows = min(g.BK, kr);
-  const auto rb = make_rsrc(p.B + static_cast<long long>(k0) * p.ldb + col0,
-                            kr > 0 ? (static_cast<long long>(krows - 1) * p.ldb + (p.N - col0)) * 4 : 0);
+    for (int j = U0; j < (U1 < NA ? U1 : NA); ++j)
+      dma_load<VEC>(ra, stage + dma_op(g, wave, j) * 64 * FPL, d.a_off[j]);
+  }
+  if constexpr (U1 > NA) {
+    const int krows = min(g.BK, kr);
+    const auto rb = make_rsrc(p.B + static_cast<long long>(k0) * p.ldb + col0,
+                              kr > 0 ? (static_cast<long long>(krows - 1) * p.ldb + (p.N - col0)) * 4 : 0);
 #pragma unroll
-  for (int j = 0; j < dma_ops_b(g, FPL); ++j)
-    dma_load<VEC>(rb, stage + g.BM * g.BK + dma_op(g, wave, j) * 64 * FPL, d.b_off[j]);
+    for (int j = (U0 > NA ? U0 : NA) - NA; j < U1 - NA; ++j)
+      dma_load<VEC>(rb, stage + g.BM * g.BK + dma_op(g, wave, j) * 64 * FPL, d.b_off[j]);
+  }
 }
 
 // Slice 0 (k in [0, r)): the same loads with elements at k >= r masked to
@@ -394,32 +401,57 @@ __device__ __forceinline__ void inner_product(const float* st, int wr0, int wc0,
   }
 }
 
-// One BK slice of the MFMA 32x32x2 inner product over a direct-LDS stage:
-// per 8-k group, one 128-bit As read per sub-tile row feeds four MFMAs
-// (k = 8*kg + 4*slot + q in MFMA q), each with its own 32-bit Bs reads.
+// Fragments of one direct-LDS k-group (8 k for 32x32x2, 16 for 16x16x4):
+// per sub-tile row one 128-bit As read (four k of the lane's row, one per
+// MFMA), per sub-tile column and MFMA one 32-bit Bs read.  MFMA q takes for
+// slot h (lane / blk) the k = group start + 4*h + q.
+template <class Cfg>
+struct DmaFrag {
+  f32x4 a[Cfg::WMITER];
+  float b[4][Cfg::WNITER];
+};
+
+template <class Cfg>
+__device__ __forceinline__ void dma_frag_load(const float* st, int kg, int wr0, int wc0, int lane,
+                                              DmaFrag<Cfg>& f) {
+  constexpr Geom g = make_geom(Cfg::tile);
+  constexpr int blk = mfma_blk(g);
+  const int fr = lane % blk, h = lane / blk;
+#pragma unroll
+  for (int wm = 0; wm < g.WMITER; ++wm)
+    f.a[wm] = *reinterpret_cast<const f32x4*>(&st[dma_as_index(g, wr0 + wm * blk + fr, dma_k(g, kg, h, 0))]);
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int wn = 0; wn < g.WNITER; ++wn)
+      f.b[q][wn] = st[dma_bs_index(g, dma_k(g, kg, h, q), wc0 + wn * blk + fr)];
+}
+
+template <class Cfg>
+__device__ __forceinline__ void dma_frag_mfma(const DmaFrag<Cfg>& f, Acc<Cfg>& acc) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int wm = 0; wm < Cfg::WMITER; ++wm)
+#pragma unroll
+      for (int wn = 0; wn < Cfg::WNITER; ++wn) {
+        if constexpr (Cfg::PATH == kPathMfma32)
+          acc.v[wm][wn] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[wm][q], f.b[q][wn], acc.v[wm][wn], 0, 0, 0);
+        else
+          acc.v[wm][wn] = __builtin_amdgcn_mfma_f32_16x16x4f32(f.a[wm][q], f.b[q][wn], acc.v[wm][wn], 0, 0, 0);
+      }
+}
+
+// One BK slice of the MFMA inner product over a direct-LDS stage.
 template <class Cfg>
 __device__ __forceinline__ void inner_product_dma(const float* st, int wr0, int wc0, int lane,
                                                   Acc<Cfg>& acc) {
   constexpr Geom g = make_geom(Cfg::tile);
-  const int fr = lane & 31, h = lane >> 5;
 #pragma unroll
-  for (int kg = 0; kg < g.BK / 8; ++kg) {
-    f32x4 a[g.WMITER];
-    float b[4][g.WNITER];
-#pragma unroll
-    for (int wm = 0; wm < g.WMITER; ++wm)
-      a[wm] = *reinterpret_cast<const f32x4*>(&st[dma_as_index(g, wr0 + wm * 32 + fr, dma_k(kg, h, 0))]);
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int wn = 0; wn < g.WNITER; ++wn) b[q][wn] = st[bs_index(g, dma_k(kg, h, q), wc0 + wn * 32 + fr)];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int wm = 0; wm < g.WMITER; ++wm)
-#pragma unroll
-        for (int wn = 0; wn < g.WNITER; ++wn)
-          acc.v[wm][wn] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[wm][q], b[q][wn], acc.v[wm][wn], 0, 0, 0);
+  for (int kg = 0; kg < g.BK / dma_kgroup(g); ++kg) {
+    DmaFrag<Cfg> f;
+    dma_frag_load<Cfg>(st, kg, wr0, wc0, lane, f);
+    dma_frag_mfma<Cfg>(f, acc);
   }
 }
 
@@ -690,13 +722,40 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
     }
     ring_barrier<kInFlight>();
     int cur = 0, nxt = S - 1;
-    for (int kt = kt0; kt < kt1; ++kt) {
-      dma_slice<Cfg, VEC>(p, d, lds + nxt * g.STAGE, row0, col0, slice_k0(kt + S - 1, r, g.BK), wave);
-      if constexpr (!(Cfg::OPT & kOptFloatLoads)) __builtin_amdgcn_sched_barrier(0);
-      inner_product_dma<Cfg>(lds + cur * g.STAGE, wr0, wc0, lane, acc);
-      ring_barrier<kInFlight>();
-      cur = cur + 1 == S ? 0 : cur + 1;
-      nxt = nxt + 1 == S ? 0 : nxt + 1;
+    if constexpr ((Cfg::OPT & kOptPipelined) != 0) {
+      // Fragments one k-group ahead; the slice's last group is multiplied
+      // after the barrier, behind the reads of the next slice's first group
+      // (those registers were read before the barrier, so the stage they
+      // came from may be refilled).  The last iteration reads one group of
+      // the stage past the segment, which is never multiplied.
+      constexpr int KG = g.BK / dma_kgroup(g);
+      DmaFrag<Cfg> f[2];
+      dma_frag_load<Cfg>(lds, 0, wr0, wc0, lane, f[0]);
+      for (int kt = kt0; kt < kt1; ++kt) {
+        dma_slice<Cfg, VEC>(p, d, lds + nxt * g.STAGE, row0, col0, slice_k0(kt + S - 1, r, g.BK), wave);
+        if constexpr (!(Cfg::OPT & kOptFloatLoads)) __builtin_amdgcn_sched_barrier(0);
+        const float* st = lds + cur * g.STAGE;
+#pragma unroll
+        for (int kg = 0; kg + 1 < KG; ++kg) {
+          dma_frag_load<Cfg>(st, kg + 1, wr0, wc0, lane, f[(kg + 1) & 1]);
+          dma_frag_mfma<Cfg>(f[kg & 1], acc);
+        }
+        ring_barrier<kInFlight>();
+        cur = cur + 1 == S ? 0 : cur + 1;
+        nxt = nxt + 1 == S ? 0 : nxt + 1;
+        dma_frag_load<Cfg>(lds + cur * g.STAGE, 0, wr0, wc0, lane, f[KG & 1]);
+        dma_frag_mfma<Cfg>(f[(KG - 1) & 1], acc);
+        if constexpr ((KG & 1) != 0) f[0] = f[1];
+      }
+    } else {
+      for (int kt = kt0; kt < kt1; ++kt) {
+        dma_slice<Cfg, VEC>(p, d, lds + nxt * g.STAGE, row0, col0, slice_k0(kt + S - 1, r, g.BK), wave);
+        if constexpr (!(Cfg::OPT & kOptFloatLoads)) __builtin_amdgcn_sched_barrier(0);
+        inner_product_dma<Cfg>(lds + cur * g.STAGE, wr0, wc0, lane, acc);
+        ring_barrier<kInFlight>();
+        cur = cur + 1 == S ? 0 : cur + 1;
+        nxt = nxt + 1 == S ? 0 : nxt + 1;
+      }
     }
     // Nothing may still be writing this workgroup's LDS when its waves end.
     if constexpr (kInFlight > 0) wait_vmem<0>();

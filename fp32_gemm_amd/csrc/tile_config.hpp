@@ -44,7 +44,10 @@ enum Opt : int {
   // MFMA paths: fragment registers double-buffered across k-steps, the next
   // slice's LDS stores placed mid-slice between MFMAs, and the next slice's
   // first fragments read right after the barrier, ahead of the current
-  // slice's last k-step.
+  // slice's last k-step.  With direct-LDS staging the unit is the k-group
+  // (one 128-bit A read per sub-tile row): its fragments are read one group
+  // ahead, and the slice's last group is multiplied after the barrier, so
+  // the matrix cores stay busy while the waves meet.
   kOptPipelined = 1,
   // Workgroup ids remapped so each XCD (the hardware hands consecutive ids to
   // the 8 XCDs in turn) works on one compact block of output tiles.
@@ -59,7 +62,7 @@ enum Opt : int {
   // of C by beta.  Those tiles' sums are therefore not bitwise reproducible
   // from run to run (they stay within the parity bound).
   kOptSplitK = 8,
-  // MFMA 32x32x2: global -> LDS with buffer loads that write LDS directly (no
+  // MFMA paths: global -> LDS with buffer loads that write LDS directly (no
   // register round-trip, no ds_write; 16-byte loads in the float4 variant,
   // 4-byte loads in the scalar variant), into an As[m][k] layout whose
   // 16-byte chunks are XOR-swizzled by row; the inner product reads four k of
@@ -140,9 +143,10 @@ enum Reason : int {
   kRegisterEstimate = 17,   // estimated registers over the per-lane budget (which shrinks
                             // when one workgroup puts several waves on each SIMD)
   kNoMfmaOnTarget = 18,
-  kBadOptions = 19,         // unknown option bits, pipelining without an even k-step count,
-                            // direct-LDS staging on another path, with pipelining, or without
-                            // BK in {8, 16, 32, 64}, or a stage ring without direct-LDS staging,
+  kBadOptions = 19,         // unknown option bits, register-staged pipelining without an even
+                            // k-step count, direct-LDS staging on the VALU path, or without
+                            // BK in {8, 16, 32, 64} (16 up for 16x16x4), or a stage ring
+                            // without direct-LDS staging,
                             // of 5 stages, or with more loads in flight than vmcnt counts, or a
                             // residency request beyond 8 waves per SIMD or the CU's LDS
   kNumReasons = 20,
@@ -186,9 +190,11 @@ constexpr int vgpr_estimate(const Tile& t, int wave) {
     return acc_per_lane(t, wave) + frags + prefetch_regs(t) + fixed;
   }
   // MFMA: fragments are one register per (sub-tile row or column, k-step);
-  // accumulators live in AccVGPRs.
-  // (With direct-LDS staging the float4 variant needs fewer registers than
-  // this; the scalar variant of the same tuple stages through registers.)
+  // accumulators live in AccVGPRs.  Direct-LDS staging holds no staged
+  // tile in registers; its fragments are a k-group's four A and four B
+  // values per sub-tile row and column, twice when pipelined.
+  if (t.opt & kOptDirectLds)  // no staging addresses either
+    return ((t.opt & kOptPipelined) ? 8 : 4) * (wmiter + t.WNITER) + fixed - 4;
   const int ksteps = (t.path == kPathMfma32) ? 2 : 1;
   return 2 * ksteps * (wmiter + t.WNITER) + prefetch_regs(t) + fixed;
 }
@@ -245,16 +251,19 @@ constexpr int check_tile(const Tile& t, const Target& m) {
       return kMfmaShape;
     // The pipelined loop alternates two fragment buffers per k-step and
     // relies on an even number of k-steps per slice.
-    if ((t.opt & kOptPipelined) && (t.BK / kstep) % 2 != 0) return kBadOptions;
+    if ((t.opt & kOptPipelined) && !(t.opt & kOptDirectLds) && (t.BK / kstep) % 2 != 0)
+      return kBadOptions;
   } else if (t.opt & kOptPipelined) {
     return kBadOptions;
   }
-  // Direct-LDS staging: MFMA 32x32x2 only, its own loop (not the pipelined
-  // one), whole 8-k groups per slice and a power-of-two number of 16-byte
-  // chunks per As row (the chunk swizzle is an XOR below that count).
+  // Direct-LDS staging: the MFMA paths, in their own loop (pipelined by
+  // k-group rather than by k-step), with whole k-groups per slice (8 k for
+  // 32x32x2, 16 for 16x16x4) and a power-of-two number of 16-byte chunks per
+  // As row (the chunk swizzle is an XOR below that count).
   if ((t.opt & kOptDirectLds) &&
-      (t.path != kPathMfma32 || (t.opt & kOptPipelined) ||
-       (t.BK != 8 && t.BK != 16 && t.BK != 32 && t.BK != 64)))
+      (t.path == kPathValu ||
+       (t.BK != 8 && t.BK != 16 && t.BK != 32 && t.BK != 64) ||
+       (t.path == kPathMfma16 && t.BK < 16)))
     return kBadOptions;
   // The stage ring belongs to the direct-LDS loop; at most 4 stages, and the
   // loads left in flight at each wait fit the 6-bit vmcnt counter.

@@ -97,7 +97,7 @@ FG_HD constexpr int bs_index(const Geom& g, int k, int n) {
   return g.BK * g.SA + k * g.SB + (n ^ swz_b(g, k));
 }
 
-// ---- direct-LDS staging (MFMA 32x32x2) ----------------------------------
+// ---- direct-LDS staging (MFMA paths) -------------------------------------
 // A buffer load that writes LDS places lane l's data at the instruction's LDS
 // base + (bytes per lane)*l: each wave instruction fills 64*FPL consecutive
 // floats, FPL = 4 for the float4 variant (16-byte loads) and 1 for the scalar
@@ -134,18 +134,37 @@ FG_HD constexpr MK dma_a_src(const Geom& g, int i, int l, int fpl) {
   const int m = f / g.BK, kk = f % g.BK;
   return MK{m, (((kk >> 2) ^ dma_sw(g, m)) << 2) | (kk & 3)};
 }
+// Bs keeps [k][n] with a column XOR per k-row.  A 32x32x2 fragment read puts
+// rows k and k+4 in different 32-lane halves, so the register-staged swz_b
+// serves; a 16x16x4 read has four 16-lane slots on rows k, k+4, k+8, k+12,
+// which the XOR (k/4 mod 2)*16 (32 banks) or (k/4 mod 4)*16 (64 banks) puts
+// on disjoint bank groups.
+FG_HD constexpr int dma_swz_b(const Geom& g, int k) {
+  return g.path != kPathMfma16 ? swz_b(g, k)
+         : g.swz == 0          ? 0
+                               : ((k >> 2) & (g.swz == 64 ? 3 : 1)) << 4;
+}
+FG_HD constexpr int dma_bs_index(const Geom& g, int k, int n) {
+  return g.BK * g.SA + k * g.SB + (n ^ dma_swz_b(g, k));
+}
 // Source of lane l in B instruction i: k-row and first column (LDS float
 // BK*BM + i*64*FPL + FPL*l of the stage).
 struct KN { int k, n; };
 FG_HD constexpr KN dma_b_src(const Geom& g, int i, int l, int fpl) {
   const int f = (i * 64 + l) * fpl;
   const int k = f / g.BN;
-  return KN{k, (f % g.BN) ^ swz_b(g, k)};
+  return KN{k, (f % g.BN) ^ dma_swz_b(g, k)};
 }
-// Fragments: the slice's k run in groups of 8; within group kg, MFMA q takes
-// for slot h (lane / 32) the k = 8*kg + 4*h + q, so one 128-bit read of As
-// (chunk 2*kg + h of the lane's row) feeds four MFMAs.
-FG_HD constexpr int dma_k(int kg, int h, int q) { return 8 * kg + 4 * h + q; }
+// Fragments: an MFMA block of blk x blk outputs takes, per lane, one A and one
+// B value for each of its slots (2 for 32x32x2, 4 for 16x16x4; slot h =
+// lane / blk).  The slice's k run in groups of 4*slots; within group kg,
+// MFMA q takes for slot h the k = 4*slots*kg + 4*h + q, so one 128-bit read
+// of As (chunk slots*kg + h of the lane's row) feeds four MFMAs.
+FG_HD constexpr int dma_slots(const Geom& g) { return g.path == kPathMfma16 ? 4 : 2; }
+FG_HD constexpr int dma_kgroup(const Geom& g) { return 4 * dma_slots(g); }
+FG_HD constexpr int dma_k(const Geom& g, int kg, int h, int q) {
+  return dma_kgroup(g) * kg + 4 * h + q;
+}
 
 // ---- waves inside the block tile -----------------------------------------
 FG_HD constexpr int wave_row0(const Geom& g, int w) { return (w / g.WAVES_N) * g.WM; }

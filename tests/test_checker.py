@@ -165,11 +165,15 @@ def test_option_guard():
     assert fg.check_tuple((128, 128, 4, 128, 64, 4, 4, 1, 128, MFMA16, 0, 1)) == 19
     assert fg.check_tuple((128, 128, 16, 64, 64, 2, 16, 1, 256, MFMA32, 32, 512)) == 19  # unknown bit
     assert fg.check_tuple((128, 128, 16, 64, 64, 2, 16, 1, 256, MFMA32, 32, 3)) == 0
-    # Direct-LDS staging: MFMA 32x32x2 only, not with the pipelined loop, and
-    # BK a power of two from 8 to 64.
+    # Direct-LDS staging: the MFMA paths only, and BK a power of two from 8 to
+    # 64 (from 16 for 16x16x4, whose k-group is 16).  Its pipeline works per
+    # k-group, so an odd k-group count (one, here) is fine.
     assert fg.check_tuple((128, 128, 16, 64, 64, 2, 16, 1, 256, MFMA32, 32, 16)) == 0
-    assert fg.check_tuple((128, 128, 16, 64, 64, 2, 16, 1, 256, MFMA32, 32, 17)) == 19
-    assert fg.check_tuple((128, 128, 16, 64, 64, 4, 4, 1, 256, MFMA16, 32, 16)) == 19
+    assert fg.check_tuple((128, 128, 16, 64, 64, 2, 16, 1, 256, MFMA32, 32, 17)) == 0
+    assert fg.check_tuple((128, 128, 8, 64, 64, 2, 16, 1, 256, MFMA32, 32, 17)) == 0
+    assert fg.check_tuple((128, 128, 16, 64, 64, 4, 4, 1, 256, MFMA16, 32, 16)) == 0
+    assert fg.check_tuple((128, 128, 16, 64, 64, 4, 4, 1, 256, MFMA16, 32, 17)) == 0
+    assert fg.check_tuple((128, 128, 8, 64, 64, 4, 4, 1, 256, MFMA16, 32, 16)) == 19
     assert fg.check_tuple((128, 64, 16, 64, 64, 2, 4, 4, 128, VALU, 32, 16)) == 19
     assert fg.check_tuple((96, 64, 24, 32, 64, 2, 16, 1, 192, MFMA32, 0, 16)) == 19
     # Stage rings (opt field 32 = 3 stages, 64 = 4): direct-LDS only, at most 4
@@ -216,6 +220,18 @@ def test_direct_lds_layout_is_conflict_free():
             assert r["status"] == 0, (t, banks, r)
             assert r["dma_read_a_ways"] == 1, (t, banks, r)
             assert r["dma_read_b_ways"] == (1 if banks == 32 else 2)
+    # 16x16x4 reads: four 16-lane slots on k-rows 4 apart; the Bs XOR by
+    # (k/4 mod 4)*16 built for 64 banks separates all four under both models,
+    # the 32-bank one (k/4 mod 2)*16 only the two a 32-bank phase serves.
+    for t in [(128, 128, 32, 64, 64, 4, 4, 1, 256, MFMA16, 64, 16),
+              (256, 256, 16, 64, 64, 4, 4, 1, 1024, MFMA16, 64, 16),
+              (128, 128, 32, 64, 64, 4, 4, 1, 256, MFMA16, 32, 16)]:
+        assert fg.check_tuple(t) == 0
+        for banks in (32, 64):
+            r = fg.simulate_tuple(t, banks=banks)
+            assert r["status"] == 0, (t, banks, r)
+            assert r["dma_read_a_ways"] == 1, (t, banks, r)
+            assert r["dma_read_b_ways"] == (1 if banks == 32 or t[10] == 64 else 2)
 
 
 @pytest.mark.parametrize("M,N", [(4096, 4096), (4097, 4095), (8192, 2048), (1000, 1500), (256, 256),
