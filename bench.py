@@ -279,20 +279,26 @@ def main():
         "parity_err": parity,
     }
     if not args.no_context:
+        # The same warm-up and launch count as the timed kernel above, so the
+        # vendor library is compared at its steady clock too.  torch.mm is
+        # the plain product (no alpha, no beta read of C).
         Cm = torch.empty_like(C0)
-        for _ in range(3):
+        mm_warm, mm_reps = max(args.warmup, 10), max(args.steps, 20)
+        for _ in range(mm_warm):
             torch.mm(Ad, Bd, out=Cm)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for _ in range(10):
+        for _ in range(mm_reps):
             torch.mm(Ad, Bd, out=Cm)
         e1.record(stream)
         torch.cuda.synchronize()
-        mm = flops / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e12
+        mm = flops / (e0.elapsed_time(e1) / mm_reps * 1e-3) / 1e12
         out["context"] = {"torch_mm_tflops": round(mm, 2),
                           "this_vs_torch_mm": round(achieved / mm, 3),
-                          "note": "vendor BLAS timing, context only; never used for dispatch or parity"}
+                          "torch_mm_launches": {"warmup": mm_warm, "timed": mm_reps},
+                          "note": "vendor BLAS timing (plain A*B), context only; never used for "
+                                  "dispatch or parity"}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, A, B, C, args.cpu_seconds)
     print(json.dumps(out), flush=True)

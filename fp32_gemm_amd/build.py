@@ -167,7 +167,13 @@ def candidates():
                  (128, 256, 32, 64, 64, 4, 4, 1, 512, MFMA16, 32),
                  (128, 128, 16, 64, 64, 4, 4, 1, 256, MFMA16, 32),
                  (128, 128, 32, 64, 64, 4, 4, 1, 256, MFMA16, 32),
-                 (128, 128, 64, 64, 32, 2, 4, 1, 512, MFMA16, 64)]:
+                 (128, 128, 64, 64, 32, 2, 4, 1, 512, MFMA16, 64),
+                 (64, 64, 64, 32, 32, 1, 16, 1, 256, MFMA32, 32),
+                 (64, 64, 32, 32, 32, 1, 16, 1, 256, MFMA32, 32),
+                 (64, 128, 32, 64, 32, 1, 16, 1, 256, MFMA32, 32),
+                 (128, 64, 32, 32, 64, 2, 16, 1, 256, MFMA32, 32),
+                 (64, 64, 64, 32, 32, 2, 4, 1, 256, MFMA16, 32),
+                 (128, 128, 64, 64, 64, 4, 4, 1, 256, MFMA16, 32)]:
         out += [base + (17,), base + (19,), base + (25,), base + (27,)]
         if base[0] * base[1] <= 128 * 128:
             out.append(base + (19 | 128,))

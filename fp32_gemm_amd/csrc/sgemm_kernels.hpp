@@ -735,15 +735,20 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
         dma_slice<Cfg, VEC>(p, d, lds + nxt * g.STAGE, row0, col0, slice_k0(kt + S - 1, r, g.BK), wave);
         if constexpr (!(Cfg::OPT & kOptFloatLoads)) __builtin_amdgcn_sched_barrier(0);
         const float* st = lds + cur * g.STAGE;
+        // The scheduling barriers keep each group's reads ahead of the
+        // previous group's MFMAs (left alone, the compiler sinks every read
+        // to just before its first use and waits for it there).
 #pragma unroll
         for (int kg = 0; kg + 1 < KG; ++kg) {
           dma_frag_load<Cfg>(st, kg + 1, wr0, wc0, lane, f[(kg + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);
           dma_frag_mfma<Cfg>(f[kg & 1], acc);
         }
         ring_barrier<kInFlight>();
         cur = cur + 1 == S ? 0 : cur + 1;
         nxt = nxt + 1 == S ? 0 : nxt + 1;
         dma_frag_load<Cfg>(lds + cur * g.STAGE, 0, wr0, wc0, lane, f[KG & 1]);
+        __builtin_amdgcn_sched_barrier(0);
         dma_frag_mfma<Cfg>(f[(KG - 1) & 1], acc);
         if constexpr ((KG & 1) != 0) f[0] = f[1];
       }
