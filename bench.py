@@ -133,7 +133,9 @@ def ladder(fg, inputs, model, w, dev, args):
     flops = model.flops(w.M, w.N, w.K)
     for rung in (1, 2, 3, 4):
         reps = max(3, min(args.steps, 20))
-        for _ in range(2):
+        # Ten warm-ups per rung: the first launches after a switch run at a
+        # lower clock.
+        for _ in range(10):
             fg.ladder(rung, Ad, Bd, Cd, w.alpha, w.beta, stream=stream)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
         torch.cuda.synchronize()

@@ -28,7 +28,7 @@ from . import binding as fg
 from . import inputs, model
 
 SHORT = (3, 10)   # warm-up, timed reps during the sweep
-LONG = (10, 50)   # re-timing of the finalists
+LONG = (20, 60)   # re-timing of the finalists
 
 
 def _time(fn, warm, reps, stream):
@@ -159,7 +159,9 @@ def main():
     ap.add_argument("--top", type=int, default=24)
     ap.add_argument("--filter", default=None,
                     help="Python expression over a config dict c (e.g. \"c['BK'] == 32\")")
-    ap.add_argument("--finalists", type=int, default=6)
+    ap.add_argument("--finalists", type=int, default=10,
+                    help="tuples re-timed interleaved with the long protocol; the sweep's "
+                         "short timings are noisier than the gaps between the best tuples")
     ap.add_argument("--best", default=None,
                     help="print the best tuple recorded for this workload in --out and exit")
     args = ap.parse_args()
