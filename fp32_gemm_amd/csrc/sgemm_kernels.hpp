@@ -228,10 +228,16 @@ __device__ __forceinline__ void dma_slice(const KernelArgs& p, const DmaLanes<Cf
   constexpr int NA = dma_ops_a(g, FPL), NB = dma_ops_b(g, FPL);
   constexpr int U0 = PART * (NA + NB) / PARTS, U1 = (PART + 1) * (NA + NB) / PARTS;
   const int kr = p.K - k0;
+  // Sizes are multiplied by an opaque 0/1 rather than selected: the compiler
+  // turns a select into a branch that duplicates the loads and cuts the loop
+  // body into separate scheduling regions.
+  int live1 = __builtin_amdgcn_readfirstlane(kr > 0 ? 1 : 0);
+  asm("" : "+s"(live1));
+  const long long live = live1;
   if constexpr (U0 < NA) {
     const int rows = min(g.BM, p.M - row0);
     const auto ra = make_rsrc(p.A + static_cast<long long>(row0) * p.lda + k0,
-                              kr > 0 ? (static_cast<long long>(rows - 1) * p.lda + kr) * 4 : 0);
+                              live * ((static_cast<long long>(rows - 1) * p.lda + kr) * 4));
 #pragma unroll
     for (int j = U0; j < (U1 < NA ? U1 : NA); ++j)
       dma_load<VEC>(ra, stage + dma_op(g, wave, j) * 64 * FPL, d.a_off[j]);
@@ -239,7 +245,7 @@ __device__ __forceinline__ void dma_slice(const KernelArgs& p, const DmaLanes<Cf
   if constexpr (U1 > NA) {
     const int krows = min(g.BK, kr);
     const auto rb = make_rsrc(p.B + static_cast<long long>(k0) * p.ldb + col0,
-                              kr > 0 ? (static_cast<long long>(krows - 1) * p.ldb + (p.N - col0)) * 4 : 0);
+                              live * ((static_cast<long long>(krows - 1) * p.ldb + (p.N - col0)) * 4));
 #pragma unroll
     for (int j = (U0 > NA ? U0 : NA) - NA; j < U1 - NA; ++j)
       dma_load<VEC>(rb, stage + g.BM * g.BK + dma_op(g, wave, j) * 64 * FPL, d.b_off[j]);
