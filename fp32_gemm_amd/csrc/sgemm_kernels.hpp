@@ -737,10 +737,16 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
       constexpr int KG = g.BK / dma_kgroup(g);
       DmaFrag<Cfg> f[2];
       dma_frag_load<Cfg>(lds, 0, wr0, wc0, lane, f[0]);
-      for (int kt = kt0; kt < kt1; ++kt) {
-        dma_slice<Cfg, VEC>(p, d, lds + nxt * g.STAGE, row0, col0, slice_k0(kt + S - 1, r, g.BK), wave);
+      // One slice with stage cs being multiplied and stage ns being loaded.
+      // With two stages the K loop runs two slices per iteration, so each
+      // one's stages are constants and its fragment reads take fixed
+      // addresses with immediate offsets (no per-slice address arithmetic).
+      // Not in the scalar variant, whose four times as many load offsets
+      // leave no registers for the second copy.
+      auto slice = [&](int kt, int cs, int ns) __attribute__((always_inline)) {
+        dma_slice<Cfg, VEC>(p, d, lds + ns * g.STAGE, row0, col0, slice_k0(kt + S - 1, r, g.BK), wave);
         if constexpr (!(Cfg::OPT & kOptFloatLoads)) __builtin_amdgcn_sched_barrier(0);
-        const float* st = lds + cur * g.STAGE;
+        const float* st = lds + cs * g.STAGE;
         // The scheduling barriers keep each group's reads ahead of the
         // previous group's MFMAs (left alone, the compiler sinks every read
         // to just before its first use and waits for it there).
@@ -751,21 +757,45 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
           dma_frag_mfma<Cfg>(f[kg & 1], acc);
         }
         ring_barrier<kInFlight>();
-        cur = cur + 1 == S ? 0 : cur + 1;
-        nxt = nxt + 1 == S ? 0 : nxt + 1;
-        dma_frag_load<Cfg>(lds + cur * g.STAGE, 0, wr0, wc0, lane, f[KG & 1]);
+        dma_frag_load<Cfg>(lds + (cs + 1 == S ? 0 : cs + 1) * g.STAGE, 0, wr0, wc0, lane, f[KG & 1]);
         __builtin_amdgcn_sched_barrier(0);
         dma_frag_mfma<Cfg>(f[(KG - 1) & 1], acc);
         if constexpr ((KG & 1) != 0) f[0] = f[1];
+      };
+      if constexpr (S == 2 && VEC) {
+        int kt = kt0;
+        for (; kt + 1 < kt1; kt += 2) {
+          slice(kt, 0, 1);
+          slice(kt + 1, 1, 0);
+        }
+        if (kt < kt1) slice(kt, 0, 1);
+      } else {
+        for (int kt = kt0; kt < kt1; ++kt) {
+          slice(kt, cur, nxt);
+          cur = cur + 1 == S ? 0 : cur + 1;
+          nxt = nxt + 1 == S ? 0 : nxt + 1;
+        }
       }
     } else {
-      for (int kt = kt0; kt < kt1; ++kt) {
-        dma_slice<Cfg, VEC>(p, d, lds + nxt * g.STAGE, row0, col0, slice_k0(kt + S - 1, r, g.BK), wave);
+      auto slice = [&](int kt, int cs, int ns) __attribute__((always_inline)) {
+        dma_slice<Cfg, VEC>(p, d, lds + ns * g.STAGE, row0, col0, slice_k0(kt + S - 1, r, g.BK), wave);
         if constexpr (!(Cfg::OPT & kOptFloatLoads)) __builtin_amdgcn_sched_barrier(0);
-        inner_product_dma<Cfg>(lds + cur * g.STAGE, wr0, wc0, lane, acc);
+        inner_product_dma<Cfg>(lds + cs * g.STAGE, wr0, wc0, lane, acc);
         ring_barrier<kInFlight>();
-        cur = cur + 1 == S ? 0 : cur + 1;
-        nxt = nxt + 1 == S ? 0 : nxt + 1;
+      };
+      if constexpr (S == 2 && VEC) {
+        int kt = kt0;
+        for (; kt + 1 < kt1; kt += 2) {
+          slice(kt, 0, 1);
+          slice(kt + 1, 1, 0);
+        }
+        if (kt < kt1) slice(kt, 0, 1);
+      } else {
+        for (int kt = kt0; kt < kt1; ++kt) {
+          slice(kt, cur, nxt);
+          cur = cur + 1 == S ? 0 : cur + 1;
+          nxt = nxt + 1 == S ? 0 : nxt + 1;
+        }
       }
     }
     // Nothing may still be writing this workgroup's LDS when its waves end.

@@ -145,7 +145,7 @@ def write_table(best_by_shape, path, defaults):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--workloads", default=",".join(inputs.WORKLOADS))
+    ap.add_argument("--workloads", default=",".join(list(inputs.WORKLOADS) + list(inputs.TUNING_EXTRA)))
     ap.add_argument("--out", default="tune_results.jsonl")
     ap.add_argument("--table-out", default=None)
     ap.add_argument("--paths", default="valu,mfma32,mfma16")
@@ -198,10 +198,11 @@ def main():
 
     bests = []
     ranked = None  # configs of the largest shape swept so far, fastest first
+    shapes = {**inputs.WORKLOADS, **inputs.TUNING_EXTRA}
     names = sorted(args.workloads.split(","), key=lambda n: model.flops(
-        inputs.WORKLOADS[n].M, inputs.WORKLOADS[n].N, inputs.WORKLOADS[n].K))
+        shapes[n].M, shapes[n].N, shapes[n].K))
     for name in names:
-        w = inputs.WORKLOADS[name]
+        w = shapes[name]
         t0 = time.time()
         use = configs[w.K % 4 == 0 and w.N % 4 == 0]
         if ranked is not None and model.flops(w.M, w.N, w.K) > args.prune_above:

@@ -142,14 +142,17 @@ typedef struct sgemm_plan_t {
 } sgemm_plan_t;
 
 /* Validates like sgemm_ex (same status codes, no device check) and fills
- * *out.  cfg_id < 0 selects the tuned configuration: the exact-shape rule,
- * else the nearest rule in (log M, log N, log K), which (from 2^30 FLOP up)
- * gives way to the nearest rule with a split-K tuple when its tile would leave
- * more than a tenth of the resident workgroup slots idle in the last wave.
+ * *out.  cfg_id < 0 selects the tuned configuration: the exact-shape rule;
+ * else, among the rules tuned on shapes that run the same variant (float4 or
+ * scalar; all rules if none does), from 2^30 FLOP up the largest block tile
+ * whose launch keeps at least 85 % of the resident workgroup slots busy (a
+ * split-K tuple's split of a partly filled last wave counted), ties going to
+ * the busier launch and then to the nearer rule in (log M, log N, log K);
+ * below that size, or when no rule fills the device, the nearest rule.
  * Split-K tiles add partial sums with atomics, so their last bits may differ
- * from run to run (within the accuracy bound).  The split
- * decision and that check need the device's compute units and occupancy;
- * without a device the nearest rule and no split are reported. */
+ * from run to run (within the accuracy bound).  The split decision and the
+ * fill check need the device's compute units and occupancy; without a device
+ * the nearest rule and no split are reported. */
 int sgemm_plan(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
                int64_t ldb, const float* C, int64_t ldc, int32_t cfg_id, sgemm_plan_t* out);
 
