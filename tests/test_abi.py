@@ -127,6 +127,38 @@ def test_tuned_table_tuples_are_compiled():
         assert tuple(int(x) for x in d.split(",")) in compiled
 
 
+def test_off_table_rules_follow_the_variant():
+    # Off the table, a shape takes a rule tuned on a shape of its own variant:
+    # the ragged rules (tuned where only the 4-byte scalar variant runs) serve
+    # unaligned shapes, the aligned rules aligned ones, even where a ragged
+    # rule's shape is nearer.  Without a device the nearest such rule is
+    # reported (the fill check needs the device's occupancy).
+    text = open(os.path.join(ROOT, "fp32_gemm_amd", "csrc", "tuned_table.inc")).read()
+    rules = {(int(M), int(N), int(K)): tuple(int(x) for x in t.split(","))
+             for M, N, K, t in re.findall(r"\{(\d+), (\d+), (\d+), \{([\d, ]+)\}\}", text)}
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("the fill check changes the choice on a device")
+    import math
+
+    def nearest(M, N, K, aligned):
+        d = {s: sum(math.log2(a / b) ** 2 for a, b in zip((M, N, K), s))
+             for s in rules if (s[2] % 4 == 0 and s[1] % 4 == 0) == aligned}
+        return rules[min(d, key=d.get)]
+
+    # 12288 x 12288 x 1024 lies a hair nearer 4097 x 4095 x 4093 than 4096^3.
+    d = {s: sum(math.log2(a / b) ** 2 for a, b in zip((12288, 12288, 1024), s))
+         for s in [(4096, 4096, 4096), (4097, 4095, 4093)]}
+    assert d[(4097, 4095, 4093)] < d[(4096, 4096, 4096)]
+    code, p = plan(12288, 12288, 1024, 1024, 12288, 12288)
+    assert code == 0 and p["vector_variant"] == 1
+    assert tuple(fg.config_info(p["cfg_id"])["tuple"]) == nearest(12288, 12288, 1024, True)
+    assert tuple(fg.config_info(p["cfg_id"])["tuple"]) != rules[(4097, 4095, 4093)]
+    code, p = plan(4000, 4001, 4003, 4003, 4001, 4001)
+    assert code == 0 and p["vector_variant"] == 0
+    assert tuple(fg.config_info(p["cfg_id"])["tuple"]) == nearest(4000, 4001, 4003, False)
+
+
 def test_quick_return_and_no_device():
     # M == 0: nothing to do, success without a device.
     assert binding.sgemm_raw(0, 4, 4, 1.0, FAKE, 4, FAKE * 2, 4, 0.0, FAKE * 4, 4) == 0
