@@ -732,20 +732,23 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
       // Fragments one k-group ahead; the slice's last group is multiplied
       // after the barrier, behind the reads of the next slice's first group
       // (those registers were read before the barrier, so the stage they
-      // came from may be refilled).  The last iteration reads one group of
-      // the stage past the segment, which is never multiplied.
+      // came from may be refilled).  The loads of slice kt+S go into that
+      // freed stage right there, among the last group's MFMAs, so they are
+      // spread over matrix work instead of stalling every wave at once, and
+      // have nearly S-1 slices to land.  The last iteration reads one group
+      // of the stage past the segment, which is never multiplied, and loads
+      // slices no one reads (zeros past K).
       constexpr int KG = g.BK / dma_kgroup(g);
       DmaFrag<Cfg> f[2];
       dma_frag_load<Cfg>(lds, 0, wr0, wc0, lane, f[0]);
-      // One slice with stage cs being multiplied and stage ns being loaded.
-      // With two stages the K loop runs two slices per iteration, so each
-      // one's stages are constants and its fragment reads take fixed
-      // addresses with immediate offsets (no per-slice address arithmetic).
-      // Not in the scalar variant, whose four times as many load offsets
-      // leave no registers for the second copy.
-      auto slice = [&](int kt, int cs, int ns) __attribute__((always_inline)) {
-        dma_slice<Cfg, VEC>(p, d, lds + ns * g.STAGE, row0, col0, slice_k0(kt + S - 1, r, g.BK), wave);
-        if constexpr (!(Cfg::OPT & kOptFloatLoads)) __builtin_amdgcn_sched_barrier(0);
+      dma_slice<Cfg, VEC>(p, d, lds + (S - 1) * g.STAGE, row0, col0, slice_k0(kt0 + S - 1, r, g.BK), wave);
+      // One slice with stage cs being multiplied.  With two stages the K
+      // loop runs two slices per iteration, so each one's stages are
+      // constants and its fragment reads take fixed addresses with immediate
+      // offsets (no per-slice address arithmetic).  Not in the scalar
+      // variant, whose four times as many load offsets leave no registers
+      // for the second copy.
+      auto slice = [&](int kt, int cs) __attribute__((always_inline)) {
         const float* st = lds + cs * g.STAGE;
         // The scheduling barriers keep each group's reads ahead of the
         // previous group's MFMAs (left alone, the compiler sinks every read
@@ -759,21 +762,21 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
         ring_barrier<kInFlight>();
         dma_frag_load<Cfg>(lds + (cs + 1 == S ? 0 : cs + 1) * g.STAGE, 0, wr0, wc0, lane, f[KG & 1]);
         __builtin_amdgcn_sched_barrier(0);
+        dma_slice<Cfg, VEC>(p, d, lds + cs * g.STAGE, row0, col0, slice_k0(kt + S, r, g.BK), wave);
         dma_frag_mfma<Cfg>(f[(KG - 1) & 1], acc);
         if constexpr ((KG & 1) != 0) f[0] = f[1];
       };
       if constexpr (S == 2 && VEC) {
         int kt = kt0;
         for (; kt + 1 < kt1; kt += 2) {
-          slice(kt, 0, 1);
-          slice(kt + 1, 1, 0);
+          slice(kt, 0);
+          slice(kt + 1, 1);
         }
-        if (kt < kt1) slice(kt, 0, 1);
+        if (kt < kt1) slice(kt, 0);
       } else {
         for (int kt = kt0; kt < kt1; ++kt) {
-          slice(kt, cur, nxt);
+          slice(kt, cur);
           cur = cur + 1 == S ? 0 : cur + 1;
-          nxt = nxt + 1 == S ? 0 : nxt + 1;
         }
       }
     } else {
@@ -799,7 +802,7 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
       }
     }
     // Nothing may still be writing this workgroup's LDS when its waves end.
-    if constexpr (kInFlight > 0) wait_vmem<0>();
+    if constexpr (kInFlight > 0 || (Cfg::OPT & kOptPipelined) != 0) wait_vmem<0>();
   } else if constexpr ((Cfg::OPT & kOptPipelined) != 0) {
     k_loop_pipelined<Cfg, VEC>(p, lds, row0, col0, t, wr0, wc0, lane, kt0, kt1, acc);
   } else {
