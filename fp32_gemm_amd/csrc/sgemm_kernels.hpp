@@ -603,31 +603,73 @@ __device__ __forceinline__ void epilogue(float* cw, int ldc, int rlim, int clim,
           }
     }
   } else {
+    // Sub-tiles in chunks of up to 32 values per lane: every load of a chunk
+    // is issued before its first store (a load cannot move above an earlier
+    // store to the same buffer), so the C read's memory latency is paid once
+    // per chunk rather than once per MFMA block.  Where three or more waves
+    // can share a SIMD's registers (the workgroup's own, times the
+    // workgroups the LDS or a residency request puts on a CU), one block at
+    // a time: the larger chunk spills there, or costs the occupancy.
     constexpr int blk = mfma_blk(g), regs = mfma_regs(g);
+    constexpr int kBlocks = g.WMITER * g.WNITER;
+    constexpr int kLdsBlocks = kGfx950.lds_bytes / lds_bytes(Cfg::tile, kGfx950);
+    constexpr int kBlocksPerCu = min_blocks_of(Cfg::tile) > kLdsBlocks ? min_blocks_of(Cfg::tile) : kLdsBlocks;
+    constexpr int kWavesPerSimd = (Cfg::NT + 255) / 256 * (kBlocksPerCu > 1 ? kBlocksPerCu : 1);
+    constexpr int kValues = kWavesPerSimd >= 3 ? regs : 32;
+    constexpr int kChunk = (kValues / regs) < 1 ? 1 : (kValues / regs) > kBlocks ? kBlocks : (kValues / regs);
     const int c_l = mfma_out_col(g, lane);
+    if constexpr (kChunk == 1) {
 #pragma unroll
-    for (int wm = 0; wm < g.WMITER; ++wm)
+      for (int wm = 0; wm < g.WMITER; ++wm)
 #pragma unroll
-      for (int wn = 0; wn < g.WNITER; ++wn) {
-        int off[regs];
-        const int c = wn * blk + c_l;
+        for (int wn = 0; wn < g.WNITER; ++wn) {
+          int off[regs];
+          const int c = wn * blk + c_l;
 #pragma unroll
-        for (int r = 0; r < regs; ++r) {
-          const int row = wm * blk + mfma_out_row(g, lane, r);
-          off[r] = (row < rlim && c < clim) ? (row * ldc + c) * 4 : kMaskedOffset;
+          for (int r = 0; r < regs; ++r) {
+            const int row = wm * blk + mfma_out_row(g, lane, r);
+            off[r] = (row < rlim && c < clim) ? (row * ldc + c) * 4 : kMaskedOffset;
+          }
+          float old[regs];
+          if (beta != 0.0f) {
+#pragma unroll
+            for (int r = 0; r < regs; ++r) old[r] = buffer_load1(rc, off[r]);
+          }
+#pragma unroll
+          for (int r = 0; r < regs; ++r) {
+            float v = alpha * acc.v[wm][wn][r];
+            if (beta != 0.0f) v = __builtin_fmaf(beta, old[r], v);
+            buffer_store1(rc, off[r], v);
+          }
         }
-        float old[regs];
-        if (beta != 0.0f) {
+      return;
+    }
+    auto offset = [&](int b, int r) {
+      const int wm = b / g.WNITER, wn = b % g.WNITER;
+      const int row = wm * blk + mfma_out_row(g, lane, r), c = wn * blk + c_l;
+      return (row < rlim && c < clim) ? (row * ldc + c) * 4 : kMaskedOffset;
+    };
 #pragma unroll
-          for (int r = 0; r < regs; ++r) old[r] = buffer_load1(rc, off[r]);
-        }
+    for (int b0 = 0; b0 < kBlocks; b0 += kChunk) {
+      constexpr int n = kChunk;
+      float old[n][regs];
+      if (beta != 0.0f) {
 #pragma unroll
-        for (int r = 0; r < regs; ++r) {
-          float v = alpha * acc.v[wm][wn][r];
-          if (beta != 0.0f) v = __builtin_fmaf(beta, old[r], v);
-          buffer_store1(rc, off[r], v);
-        }
+        for (int b = 0; b < n; ++b)
+#pragma unroll
+          for (int r = 0; r < regs; ++r)
+            if (b0 + b < kBlocks) old[b][r] = buffer_load1(rc, offset(b0 + b, r));
       }
+#pragma unroll
+      for (int b = 0; b < n; ++b)
+#pragma unroll
+        for (int r = 0; r < regs; ++r) {
+          if (b0 + b >= kBlocks) continue;
+          float v = alpha * acc.v[(b0 + b) / g.WNITER][(b0 + b) % g.WNITER][r];
+          if (beta != 0.0f) v = __builtin_fmaf(beta, old[b][r], v);
+          buffer_store1(rc, offset(b0 + b, r), v);
+        }
+    }
   }
 }
 
