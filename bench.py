@@ -70,10 +70,18 @@ def cpu_baseline(w, A, B, C, target_s):
     t0 = time.perf_counter()
     oracle.sgemm(A[:rows], B, C[:rows], w.alpha, w.beta)
     dt = time.perf_counter() - t0
-    gflops = 2.0 * rows * w.N * w.K / dt / 1e9
+    # Where the whole product takes well under the target, repeat it (the
+    # same call on the same inputs) until about the target has been spent.
+    passes = 1
+    while rows == w.M and dt < 0.9 * target_s and dt / passes < target_s:
+        oracle.sgemm(A, B, C, w.alpha, w.beta)
+        passes += 1
+        dt = time.perf_counter() - t0
+    gflops = 2.0 * rows * w.N * w.K * passes / dt / 1e9
+    what = (f"first {rows} of {w.M} rows of the same {w.M}x{w.N}x{w.K} product" if rows < w.M
+            else f"the whole {w.M}x{w.N}x{w.K} product, {passes} pass{'es' if passes > 1 else ''}")
     return {"value": round(gflops, 3), "unit": "GFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {rows} of {w.M} rows of the same {w.M}x{w.N}x{w.K} product "
-                      f"(fp64 accumulation, OpenMP over rows), {dt:.1f} s"}
+            "sample": f"{what} (fp64 accumulation, OpenMP over rows), {dt:.1f} s"}
 
 
 def oracle_timing(inputs, model, max_seconds=20.0):
