@@ -53,14 +53,19 @@ WORKLOADS = {
     ]
 }
 
-# Extra aligned shapes the autotuner records rules for, between the graded
-# workloads, where the last wave of the 4096^3 tile is poorly filled (not
-# graded, no parity bar of their own beyond the sweep's exact check).
+# Extra aligned shapes the autotuner records rules for: between the graded
+# workloads, where no graded rule's tile fills the device's resident slots,
+# and two skinny products (not graded, no parity bar of their own beyond the
+# sweep's exact check).
 TUNING_EXTRA = {
     w.name: w
     for w in [
         Workload("sq3072", 3072, 3072, 3072, "uniform", "uniform", 0.5, 3.0, 9),
         Workload("sq5120", 5120, 5120, 5120, "uniform", "uniform", 0.5, 3.0, 10),
+        Workload("sq1536", 1536, 1536, 1536, "uniform", "uniform", 0.5, 3.0, 11),
+        Workload("sq2560", 2560, 2560, 2560, "uniform", "uniform", 0.5, 3.0, 12),
+        Workload("skinny64x8192x8192", 64, 8192, 8192, "uniform", "uniform", 0.5, 3.0, 13),
+        Workload("skinny8192x64x8192", 8192, 64, 8192, "uniform", "uniform", 0.5, 3.0, 14),
     ]
 }
 
