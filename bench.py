@@ -164,8 +164,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} "
-              f"(WORLD_SIZE={world}) is not supported", file=sys.stderr, flush=True)
+        print(f"bench.py: the benchmark runs the single-GPU kernel on exactly one GPU; "
+              f"--gpus {args.gpus} (WORLD_SIZE={world}) is not supported", file=sys.stderr, flush=True)
         sys.exit(2)
 
     if args.oracle_timing:
