@@ -282,6 +282,24 @@ def test_workload(fg, dev, orc, name):
     log(f"[workload] {name} err={err:.3e}")
 
 
+@pytest.mark.parametrize("name", list(inputs.TUNING_EXTRA))
+def test_tuning_only_shape(fg, dev, orc, name):
+    # The dispatch table's tuning-only shapes run their own rule's tuple
+    # (split-K for most): sampled outputs against the oracle, C outside the
+    # window untouched.
+    w = inputs.TUNING_EXTRA[name]
+    log(f"[tuning shape] {name} {w.M}x{w.N}x{w.K} alpha={w.alpha} beta={w.beta}")
+    A, B, C = inputs.make(w)
+    cv = run(fg, dev, A, B, C, w.alpha, w.beta, ldc_pad=0, guard=2)
+    got = cv.result()
+    assert cv.untouched()
+    rows, cols = inputs.sample_indices(w.M, w.N, 3000, seed=w.seed)
+    _, e64 = orc.entries(rows, cols, A, B, C, w.alpha, w.beta)
+    err = _err(got[rows, cols], e64, w.K, A, B)
+    log(f"[tuning shape] {name} err={err:.3e}")
+    assert err <= TOL, f"{name}: sampled err={err}"
+
+
 @pytest.mark.parametrize("shape", [(4097, 4095, 4093), (1000, 1500, 777), (4096, 4096, 4096)])
 def test_integer_inputs_bit_exact_full_size(fg, dev, orc, shape):
     M, N, K = shape
