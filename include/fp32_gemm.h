@@ -112,15 +112,17 @@ typedef struct sgemm_config_t {
   int32_t path;
   int32_t BM, BN, BK, WM, WN, WNITER, TM, TN, NT;
   int32_t swz; /* 0 = unswizzled LDS, 32 or 64 = XOR swizzle for that bank count */
-  int32_t opt; /* schedule options: bit 0 pipelined MFMA loop, bit 1 XCD-aware tile order,
-                  bit 2 unpinned global loads, bit 3 split-K for a partly filled last wave
-                  (those tiles accumulate with fp32 atomics: not bitwise reproducible),
-                  bit 4 direct global-to-LDS loads (MFMA 32x32x2; 16-byte loads in the
-                  float4 variant, 4-byte loads in the scalar one), bits 5-6 with bit 4:
-                  LDS stages - 2, bits 7-8: workgroups per CU requested - 1 (0 = none) */
+  int32_t opt; /* schedule options: bit 0 pipelined MFMA loop (fragments read one k-step,
+                  or with bit 4 one k-group, ahead of the MFMAs), bit 1 XCD-aware tile
+                  order, bit 2 unpinned global loads, bit 3 split-K for a partly filled
+                  last wave (those tiles accumulate with fp32 atomics: not bitwise
+                  reproducible), bit 4 direct global-to-LDS loads (both MFMA paths;
+                  16-byte loads in the float4 variant, 4-byte loads in the scalar one),
+                  bits 5-6 with bit 4: LDS stages - 2, bits 7-8: workgroups per CU
+                  requested - 1 (0 = none) */
   int32_t WMITER, WSUBM, WSUBN;
   int32_t acc_per_lane;
-  int32_t lds_bytes;     /* both LDS stages */
+  int32_t lds_bytes;     /* all LDS stages */
   int32_t vgpr_estimate; /* the checker's estimate; the compiler report is authoritative */
 } sgemm_config_t;
 
