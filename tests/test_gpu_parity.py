@@ -207,11 +207,13 @@ def test_direct_lds_configs_short_and_ragged_K(fg, dev, orc, variant):
     # Direct-to-LDS configs run their K slices partial-first: slice 0 holds the
     # K % BK remainder (masked in both operands) and every later slice is
     # whole.  K = 0 (no slice), K below one slice, a one-column tail and a
-    # tail one past a whole slice, on ragged M and N, for both load widths.
+    # tail one past a whole slice, on ragged M and N, for both load widths;
+    # K = 196 / 197 gives BK = 64 tiles an even slice count and BK = 32 an
+    # odd one (the two-slice K loop and its one-slice tail).
     cfgs = [c for c in fg.configs() if c["opt"] & 16]
     N = 92 if variant == "vec" else 91
     pad = 4 if variant == "vec" else 5
-    for K in ((0, 4, 36, 64) if variant == "vec" else (0, 1, 33, 65)):
+    for K in ((0, 4, 36, 64, 196) if variant == "vec" else (0, 1, 33, 65, 197)):
         log(f"[direct-lds] {variant} 70x{N}x{K}: {len(cfgs)} configs")
         if K == 0:
             C = inputs.make_random(70, N, 1, seed=1700)[2]
