@@ -405,6 +405,57 @@ def test_alpha_zero_and_beta_zero(fg, dev, orc):
     assert np.array_equal(cv.result(), cv0.result())
 
 
+def _nonfinite_like(C):
+    bad = np.full(C.shape, np.nan, dtype=np.float32)
+    bad.reshape(-1)[1::3] = np.inf
+    bad.reshape(-1)[2::3] = -np.inf
+    return bad
+
+
+def test_beta_zero_never_reads_C(fg, dev, orc):
+    """With beta == 0 the old C is not read, so NaN and infinities in it must
+    not reach the result.  One configuration of every (path, options) class
+    in both variants on ragged shapes, a split-K configuration whose tail is
+    split (the pre-pass writes zeros), the default dispatch, and K == 0
+    (an empty sum: zeros).  Integer inputs, so each result is exact."""
+    for M, N, K in (SHAPE_VEC, SHAPE_SCALAR):
+        A, B, C = inputs.make_small_int(M, N, K, seed=41 + M)
+        want, _ = orc.sgemm(A, B, np.zeros_like(C), 0.5, 0.0)
+        bad = _nonfinite_like(C)
+        seen = {}
+        for c in fg.configs():
+            seen.setdefault((c["path"], c["opt"]), c["id"])
+        for cfg in [-1] + sorted(seen.values()):
+            cv = run(fg, dev, A, B, bad, 0.5, 0.0, cfg=cfg)
+            assert cv.untouched(), f"cfg {cfg}: wrote outside C"
+            got = cv.result()
+            assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (M, N, K, cfg)
+        log(f"[beta0] {M}x{N}x{K}: {len(seen)} configuration classes")
+    M, N, K = 4097, 4095, 130
+    A, B, C = inputs.make_small_int(M, N, K, seed=43)
+    rows, cols = inputs.sample_indices(M, N, 2000, seed=44)
+    e32, _ = orc.entries(rows, cols, A, B, np.zeros_like(C), 0.5, 0.0)
+    split = None
+    for c in fg.configs():
+        if c["opt"] & 8:
+            plan = fg.plan(M, N, K, 1 << 40, K, 2 << 40, N, 4 << 40, N, c["id"])
+            if plan["splits"] > 1 and plan["tiles_full"] > 0:
+                split = c["id"]
+                break
+    assert split is not None, "no configuration split a tail"
+    for cfg in (split, -1):
+        cv = run(fg, dev, A, B, _nonfinite_like(C), 0.5, 0.0, cfg=cfg, ldc_pad=0, guard=1)
+        assert cv.untouched()
+        got = cv.result()
+        assert np.array_equal(got[rows, cols].view(np.uint32), e32.view(np.uint32)), cfg
+        assert np.isfinite(got).all(), cfg
+    cv = Canvas(_nonfinite_like(np.zeros((70, 90), np.float32)), 95, 2, dev)
+    fg.sgemm(torch.empty((70, 0), device=dev), torch.empty((0, 90), device=dev), cv.view, 0.5, 0.0)
+    torch.cuda.synchronize()
+    assert cv.untouched()
+    assert np.array_equal(cv.result(), np.zeros((70, 90), np.float32))
+
+
 def test_alpha_beta_linearity(fg, dev, orc):
     M, N, K = 384, 320, 256
     A, B, C = inputs.make_random(M, N, K, seed=8)
