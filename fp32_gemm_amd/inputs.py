@@ -114,6 +114,21 @@ def make_small_int(M, N, K, seed, lo=-4, hi=4):
     return A, B, C
 
 
+def make_small_int_device(M, N, K, seed, device, lo=-4, hi=4):
+    """make_small_int's distribution drawn on a GPU by a seeded torch
+    generator, for operands of several GiB each that would take minutes to
+    draw and copy from the host.  Returns float32 tensors (A, B, C) on
+    `device`; a check copies back only the rows and columns it samples."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+
+    def draw(shape):
+        return torch.randint(lo, hi + 1, shape, generator=g, device=device, dtype=torch.float32)
+
+    return draw((M, K)), draw((K, N)), draw((M, N))
+
+
 def sample_indices(M, N, count, seed, tile=(256, 256)):
     """Output positions for sampled checks at sizes the CPU oracle cannot
     finish in full: random entries plus every tile corner and the last row and

@@ -319,6 +319,46 @@ def test_integer_inputs_bit_exact_full_size(fg, dev, orc, shape):
     assert np.array_equal(got[rows, cols].view(np.uint32), e32.view(np.uint32))
 
 
+def test_operands_beyond_4GiB(fg, dev, orc):
+    """Every operand spans more than 2^32 bytes, so tile base addresses lie
+    past what a 32-bit buffer offset reaches (the kernels form bases in 64
+    bits and keep only in-tile offsets in 32).  Default dispatch in both
+    variants; sampled outputs, including the rows just past each 4 GiB
+    boundary of A and C (every output reads B's last rows, which lie past
+    it), bit-exact against the oracle on integer inputs; the guard rows and
+    padding columns around C unchanged."""
+    M, N, K, pad = 32800, 32900, 32780, 4
+    A, B, Cin = inputs.make_small_int_device(M, N, K, seed=55, device=dev)
+    big = torch.full((M + 2, N + pad), CANARY, dtype=torch.int32, device=dev)
+    Cv = big.view(torch.float32)[1:1 + M, :N]
+    assert min(M * K, K * N, M * (N + pad)) * 4 > 1 << 32
+    rng = np.random.default_rng(56)
+    ra, rc = (1 << 32) // (4 * K), (1 << 32) // (4 * (N + pad))
+    rows = sorted({0, 1, 255, 256, ra - 1, ra, ra + 1, rc - 1, rc, rc + 1, M - 2, M - 1}
+                  | set(rng.integers(0, M, 20).tolist()))
+    cols = sorted({0, 255, 256, N - 5, N - 2, N - 1} | set(rng.integers(0, N, 26).tolist()))
+    ri, ci = (x.ravel() for x in np.meshgrid(np.arange(len(rows)), np.arange(len(cols)), indexing="ij"))
+    rt, ct = torch.tensor(rows, device=dev), torch.tensor(cols, device=dev)
+    for variant, A_, B_ in (("vec", A, B), ("scalar", A[:, 1:], B[1:, :])):
+        Kv = A_.shape[1]
+        Cv.copy_(Cin)
+        pl = fg.plan(M, N, Kv, A_.data_ptr(), K, B_.data_ptr(), N, Cv.data_ptr(), N + pad)
+        log(f"[4GiB] {variant} {M}x{N}x{Kv}: cfg {pl['cfg_id']} vector={pl['vector_variant']}")
+        assert pl["vector_variant"] == (variant == "vec")
+        Asub = A_.index_select(0, rt).cpu().numpy()
+        Bsub = B_.index_select(1, ct).cpu().numpy()
+        Csub = Cin.index_select(0, rt).index_select(1, ct).cpu().numpy()
+        e32, _ = orc.entries(ri, ci, Asub, Bsub, Csub, 0.5, 3.0)
+        fg.sgemm_ex(A_, B_, Cv, 0.5, 3.0)
+        torch.cuda.synchronize()
+        got = Cv.index_select(0, rt).index_select(1, ct).cpu().numpy()
+        assert np.array_equal(got[ri, ci].view(np.uint32), e32.view(np.uint32)), variant
+        assert bool((big[0] == CANARY).all()) and bool((big[M + 1] == CANARY).all())
+        assert bool((big[:, N:] == CANARY).all()), variant
+    del A, B, Cin, big, Cv
+    torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------------------
 # Closed forms at full size.
 
