@@ -304,9 +304,39 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         mm = flops / (e0.elapsed_time(e1) / mm_reps * 1e-3) / 1e12
+        # Cold caches: a 512 MiB write between launches evicts A, B and C
+        # from the L2s and the 256 MiB Infinity Cache; each launch is timed
+        # alone, on a pristine C written before the eviction.  Three untimed
+        # launches before each eviction hold the clock: isolated launches
+        # after a synchronisation otherwise start ~25 % slower and take about
+        # thirty launches to recover, whatever the caches hold.
+        scratch = torch.empty(128 << 20, dtype=torch.float32, device=dev)
+        spare = torch.empty_like(C0)
+
+        def cold_times(f):
+            t = []
+            for i in range(10):
+                Cs[i % pool].copy_(C0)
+                for _ in range(3):
+                    f(spare)
+                scratch.fill_(float(i))
+                e0.record(stream)
+                f(Cs[i % pool])
+                e1.record(stream)
+                torch.cuda.synchronize()
+                t.append(e0.elapsed_time(e1))
+            return float(np.median(t))
+
+        cold_ms = cold_times(lambda Cx: fg.sgemm_ex(Ad, Bd, Cx, w.alpha, w.beta, stream=stream,
+                                                    cfg_id=args.cfg))
+        cold_mm_ms = cold_times(lambda Cx: torch.mm(Ad, Bd, out=Cx))
+        del scratch, spare
         out["context"] = {"torch_mm_tflops": round(mm, 2),
                           "this_vs_torch_mm": round(achieved / mm, 3),
                           "torch_mm_launches": {"warmup": mm_warm, "timed": mm_reps},
+                          "cold_cache_tflops": round(flops / (cold_ms * 1e-3) / 1e12, 2),
+                          "cold_cache_ms_median": round(cold_ms, 4),
+                          "torch_mm_cold_cache_tflops": round(flops / (cold_mm_ms * 1e-3) / 1e12, 2),
                           "note": "vendor BLAS timing (plain A*B), context only; never used for "
                                   "dispatch or parity"}
     if not args.no_cpu_baseline:
