@@ -210,12 +210,16 @@ def _operand(t, name):
         raise TypeError(f"{name} must be float32, got {t.dtype}")
     if t.dim() != 2:
         raise ValueError(f"{name} must be 2-D")
-    if t.device.type != "cuda":
-        raise ValueError(f"{name} must be on a GPU device")
     if t.shape[1] > 1 and t.stride(1) != 1:
         raise ValueError(f"{name} must have unit column stride (row-major)")
-    ld = t.stride(0) if t.shape[0] > 1 else max(t.shape[1], 1)
-    return t.data_ptr(), max(ld, t.shape[1], 1)
+    if t.shape[0] > 1 and t.shape[1] > 0 and t.stride(0) < t.shape[1]:
+        # Expanded or otherwise overlapping rows: no leading dimension
+        # describes them, and the kernels would read past the storage.
+        raise ValueError(f"{name}: rows overlap (row stride {t.stride(0)} < {t.shape[1]} columns)")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
+    ld = t.stride(0) if t.shape[0] > 1 else t.shape[1]
+    return t.data_ptr(), max(ld, 1)
 
 
 def sgemm_ex(A, B, C, alpha=1.0, beta=0.0, stream=None, cfg_id=-1):

@@ -209,3 +209,21 @@ def test_ladder_argument_handling():
     import torch
     if not torch.cuda.is_available():
         assert f(1, 4, 4, 4, 1.0, FAKE, 4, FAKE * 2, 4, 0.0, FAKE * 4, 4, None) == 1
+
+
+def test_binding_rejects_overlapping_rows():
+    """Expanded or overlapping rows have no leading dimension; the binding
+    refuses them instead of describing them as a dense matrix (which would
+    make the kernels read past the storage)."""
+    import torch
+    with pytest.raises(ValueError, match="overlap"):
+        binding._operand(torch.zeros(1, 8).expand(4, 8), "A")
+    with pytest.raises(ValueError, match="overlap"):
+        binding._operand(torch.zeros(64).as_strided((4, 8), (4, 1)), "C")
+    with pytest.raises(ValueError, match="column stride"):
+        binding._operand(torch.zeros(8, 4).t(), "B")
+    # A row slice of a wider buffer and a single expanded row are valid
+    # layouts: they pass every layout check and stop at the device check.
+    for ok in (torch.zeros(4, 12)[:, :8], torch.zeros(1, 8).expand(1, 8), torch.zeros(5, 1)):
+        with pytest.raises(ValueError, match="GPU device"):
+            binding._operand(ok, "B")
