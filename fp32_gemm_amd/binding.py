@@ -262,6 +262,8 @@ def ladder(rung, A, B, C, alpha=1.0, beta=0.0, stream=None):
     N = B.shape[1]
     if B.shape[0] != K or tuple(C.shape) != (M, N):
         raise ValueError("shape mismatch")
+    if not (A.device == B.device == C.device):
+        raise ValueError("A, B and C must be on the same device")
     if stream is None:
         stream = torch.cuda.current_stream(C.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
