@@ -36,7 +36,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
-    ap.add_argument("--no-context", action="store_true", help="skip timing torch.mm")
+    ap.add_argument("--no-context", action="store_true", help="skip the context timings (torch.mm, cold caches)")
     ap.add_argument("--ladder", action="store_true",
                     help="only time the four ladder rungs on the workload (one JSON line)")
     ap.add_argument("--oracle-timing", action="store_true",
