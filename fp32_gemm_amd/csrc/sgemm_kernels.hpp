@@ -252,6 +252,34 @@ __device__ __forceinline__ void dma_slice(const KernelArgs& p, const DmaLanes<Cf
   }
 }
 
+// Past the K segment the ring has nothing left to fetch: the last slices'
+// loads bring band `band` (32-row bands, float4 variant) of this wave's C
+// tile into the caches instead, through the freed stage (never read), so the
+// epilogue's first reads of C hit.  With beta == 0 the resource is empty.
+template <class Cfg>
+__device__ __forceinline__ void dma_c_band(const KernelArgs& p, float* stage, int crow0, int ccol0,
+                                           int band, int wave, int lane) {
+  constexpr Geom g = make_geom(Cfg::tile);
+  constexpr int NA = dma_ops_a(g, 4), NB = dma_ops_b(g, 4);
+  constexpr int LPR = g.WN / 4;            // lanes per wave-tile row
+  constexpr int RPO = 64 / LPR;            // rows per load
+  static_assert(g.WN % 4 == 0 && 64 % LPR == 0, "wave-tile row width");
+  const int rows = min(g.WM, p.M - crow0), cols = min(g.WN, p.N - ccol0);
+  int live1 = __builtin_amdgcn_readfirstlane((p.beta != 0.0f && rows > 0 && cols > 0) ? 1 : 0);
+  asm("" : "+s"(live1));
+  const long long live = live1;
+  const auto rc = make_rsrc(p.C + static_cast<long long>(crow0) * p.ldc + ccol0,
+                            live * ((static_cast<long long>(rows - 1) * p.ldc + cols) * 4));
+  const int ldc = static_cast<int>(p.ldc);
+#pragma unroll
+  for (int j = 0; j < NA + NB; ++j) {
+    const int r = band * (NA + NB) * RPO + j * RPO + lane / LPR, c = (lane % LPR) * 4;
+    const int off = (r < rows && c < cols) ? (r * ldc + c) * 4 : kMaskedOffset;
+    float* dst = j < NA ? stage + dma_op(g, wave, j) * 256 : stage + g.BM * g.BK + dma_op(g, wave, j - NA) * 256;
+    dma_load<true>(rc, dst, off);
+  }
+}
+
 // Slice 0 (k in [0, r)): the same loads with elements at k >= r masked to
 // zero in both operands (so nothing past K, even a non-finite value, meets a
 // valid term).  In the float4 variant r % 4 == 0, so a float4 is wholly
@@ -778,8 +806,10 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
       // freed stage right there, among the last group's MFMAs, so they are
       // spread over matrix work instead of stalling every wave at once, and
       // have nearly S-1 slices to land.  The last iteration reads one group
-      // of the stage past the segment, which is never multiplied, and loads
-      // slices no one reads (zeros past K).
+      // of the stage past the segment, which is never multiplied; the last S
+      // slices have no slice left to load, and load either nothing (zeros
+      // past K) or, in the float4 variant of the 32x32 path, bands of the
+      // wave's C tile that the epilogue reads first (dma_c_band).
       constexpr int KG = g.BK / dma_kgroup(g);
       DmaFrag<Cfg> f[2];
       dma_frag_load<Cfg>(lds, 0, wr0, wc0, lane, f[0]);
@@ -790,7 +820,7 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
       // offsets (no per-slice address arithmetic).  Not in the scalar
       // variant, whose four times as many load offsets leave no registers
       // for the second copy.
-      auto slice = [&](int kt, int cs) __attribute__((always_inline)) {
+      auto slice = [&](int kt, int cs, bool c_band = false) __attribute__((always_inline)) {
         const float* st = lds + cs * g.STAGE;
         // The scheduling barriers keep each group's reads ahead of the
         // previous group's MFMAs (left alone, the compiler sinks every read
@@ -804,17 +834,27 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
         ring_barrier<kInFlight>();
         dma_frag_load<Cfg>(lds + (cs + 1 == S ? 0 : cs + 1) * g.STAGE, 0, wr0, wc0, lane, f[KG & 1]);
         __builtin_amdgcn_sched_barrier(0);
-        dma_slice<Cfg, VEC>(p, d, lds + cs * g.STAGE, row0, col0, slice_k0(kt + S, r, g.BK), wave);
+        if constexpr (VEC && Cfg::PATH == kPathMfma32) {
+          if (c_band)
+            dma_c_band<Cfg>(p, lds + cs * g.STAGE, row0 + wr0, col0 + wc0, kt + S - kt1, wave, lane);
+          else
+            dma_slice<Cfg, VEC>(p, d, lds + cs * g.STAGE, row0, col0, slice_k0(kt + S, r, g.BK), wave);
+        } else {
+          dma_slice<Cfg, VEC>(p, d, lds + cs * g.STAGE, row0, col0, slice_k0(kt + S, r, g.BK), wave);
+        }
         dma_frag_mfma<Cfg>(f[(KG - 1) & 1], acc);
         if constexpr ((KG & 1) != 0) f[0] = f[1];
       };
       if constexpr (S == 2 && VEC) {
         int kt = kt0;
-        for (; kt + 1 < kt1; kt += 2) {
+        // Pairs while both slices still load real data; the last two or
+        // three slices run one at a time, and those past the segment's end
+        // prefetch C instead (float4 variant of the 32x32 path).
+        for (; kt + 3 < kt1; kt += 2) {
           slice(kt, 0);
           slice(kt + 1, 1);
         }
-        if (kt < kt1) slice(kt, 0);
+        for (; kt < kt1; ++kt) slice(kt, (kt - kt0) & 1, kt + S >= kt1);
       } else {
         for (int kt = kt0; kt < kt1; ++kt) {
           slice(kt, cur);
