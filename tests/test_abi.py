@@ -227,3 +227,26 @@ def test_binding_rejects_overlapping_rows():
     for ok in (torch.zeros(4, 12)[:, :8], torch.zeros(1, 8).expand(1, 8), torch.zeros(5, 1)):
         with pytest.raises(ValueError, match="GPU device"):
             binding._operand(ok, "B")
+
+
+CLIENT = os.path.join(ROOT, "tests", "c_client", "sgemm_client")
+
+
+def test_header_is_strict_c99():
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only",
+                    "-x", "c", HEADER], check=True)
+
+
+def test_c_client_device_free_calls():
+    """A plain C program built against the header and the library (built by
+    __graft_entry__.build()) sees the same configuration table, plan and
+    status strings as the Python binding."""
+    if not os.path.exists(CLIENT):
+        pytest.fail("tests/c_client/sgemm_client is missing: run __graft_entry__.build()")
+    out = subprocess.run([CLIENT, "info"], capture_output=True, text=True, check=True, timeout=60).stdout
+    assert int(re.search(r"^configs (\d+)$", out, flags=re.M).group(1)) == fg.num_configs()
+    m = re.search(r"^plan (-?\d+) cfg (\d+) vector (\d+) grid (\d+) block (\d+)$", out, flags=re.M)
+    p = binding.plan(4096, 4096, 4096, FAKE, 4096, FAKE * 2, 4096, FAKE * 4, 4096)
+    assert (int(m.group(1)), int(m.group(2)), int(m.group(3)), int(m.group(4)), int(m.group(5))) == \
+        (0, p["cfg_id"], p["vector_variant"], p["grid"], p["block"])
+    assert f"status -6 {fg.status_string(-6)}" in out

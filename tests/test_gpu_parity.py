@@ -4,6 +4,7 @@ Bar: max|C_gpu - C64| / (K * max|A| * max|B|) <= 1e-6, bit-exact equality on
 inputs whose sums are exact in fp32 (small integers, identity, all-ones,
 rank-1), and every byte of C outside the M x N window untouched.
 """
+import os
 import sys
 
 import numpy as np
@@ -357,6 +358,29 @@ def test_operands_beyond_4GiB(fg, dev, orc):
         assert bool((big[:, N:] == CANARY).all()), variant
     del A, B, Cin, big, Cv
     torch.cuda.empty_cache()
+
+
+def test_c_client_runs_sgemm(dev, orc, tmp_path):
+    """The library from plain C: a C99 program (tests/c_client) copies
+    integer-valued inputs to hipMalloc'd buffers and calls sgemm() on the
+    null stream, no Python or torch on that path; bit-exact against the
+    oracle."""
+    import subprocess
+    client = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_client", "sgemm_client")
+    if not os.path.exists(client):
+        pytest.fail("tests/c_client/sgemm_client is missing: run __graft_entry__.build()")
+    M, N, K = 333, 260, 129
+    A, B, C = inputs.make_small_int(M, N, K, seed=61)
+    files = [str(tmp_path / f"{n}.bin") for n in ("A", "B", "C", "out")]
+    for x, f in zip((A, B, C), files):
+        x.tofile(f)
+    log(f"[c client] {M}x{N}x{K}")
+    r = subprocess.run([client, "run", str(M), str(N), str(K), "0.5", "3", *files],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    got = np.fromfile(files[3], dtype=np.float32).reshape(M, N)
+    want, _ = orc.sgemm(A, B, C, 0.5, 3.0)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
 
 
 # ---------------------------------------------------------------------------
