@@ -808,9 +808,14 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
       // have nearly S-1 slices to land.  The last iteration reads one group
       // of the stage past the segment, which is never multiplied; the last S
       // slices have no slice left to load, and load either nothing (zeros
-      // past K) or, in the float4 variant of the 32x32 path, bands of the
-      // wave's C tile that the epilogue reads first (dma_c_band).
+      // past K) or, on the 32x32 path's 256x256 tiles in the float4 variant,
+      // bands of the wave's C tile that the epilogue reads first
+      // (dma_c_band).
       constexpr int KG = g.BK / dma_kgroup(g);
+      // The C prefetch of the last slices pays on the 256x256 tiles of the
+      // 32x32 path (one long K loop per tile, C read after it); on smaller
+      // tiles the one-at-a-time tail it needs costs more than it saves.
+      constexpr bool kCPrefetch = VEC && S == 2 && Cfg::PATH == kPathMfma32 && g.BM * g.BN >= 256 * 256;
       DmaFrag<Cfg> f[2];
       dma_frag_load<Cfg>(lds, 0, wr0, wc0, lane, f[0]);
       dma_slice<Cfg, VEC>(p, d, lds + (S - 1) * g.STAGE, row0, col0, slice_k0(kt0 + S - 1, r, g.BK), wave);
@@ -834,7 +839,7 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
         ring_barrier<kInFlight>();
         dma_frag_load<Cfg>(lds + (cs + 1 == S ? 0 : cs + 1) * g.STAGE, 0, wr0, wc0, lane, f[KG & 1]);
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (VEC && Cfg::PATH == kPathMfma32) {
+        if constexpr (kCPrefetch) {
           if (c_band)
             dma_c_band<Cfg>(p, lds + cs * g.STAGE, row0 + wr0, col0 + wc0, kt + S - kt1, wave, lane);
           else
@@ -845,16 +850,23 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
         dma_frag_mfma<Cfg>(f[(KG - 1) & 1], acc);
         if constexpr ((KG & 1) != 0) f[0] = f[1];
       };
-      if constexpr (S == 2 && VEC) {
+      if constexpr (S == 2 && VEC && kCPrefetch) {
         int kt = kt0;
         // Pairs while both slices still load real data; the last two or
         // three slices run one at a time, and those past the segment's end
-        // prefetch C instead (float4 variant of the 32x32 path).
+        // prefetch C instead.
         for (; kt + 3 < kt1; kt += 2) {
           slice(kt, 0);
           slice(kt + 1, 1);
         }
         for (; kt < kt1; ++kt) slice(kt, (kt - kt0) & 1, kt + S >= kt1);
+      } else if constexpr (S == 2 && VEC) {
+        int kt = kt0;
+        for (; kt + 1 < kt1; kt += 2) {
+          slice(kt, 0);
+          slice(kt + 1, 1);
+        }
+        if (kt < kt1) slice(kt, 0);
       } else {
         for (int kt = kt0; kt < kt1; ++kt) {
           slice(kt, cur);
