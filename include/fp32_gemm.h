@@ -146,12 +146,14 @@ typedef struct sgemm_plan_t {
 /* Validates like sgemm_ex (same status codes, no device check) and fills
  * *out.  cfg_id < 0 selects the tuned configuration: the exact-shape rule;
  * else, among the rules tuned on shapes that run the same variant (float4 or
- * scalar; all rules if none does), from 2^30 FLOP up the largest block tile
- * whose launch keeps at least 85 % of the resident workgroup slots busy (a
+ * scalar; all rules if none does), from 2^30 FLOP up and with K >= 256 the
+ * largest block tile whose launch keeps at least 85 % of the resident
+ * workgroup slots busy (a
  * split-K tuple's split of a partly filled last wave counted; a launch that
  * would split every tile does not count as filling), ties going to
  * the busier launch and then to the nearer rule in (log M, log N, log K);
- * below that size, or when no rule fills the device, the nearest rule.
+ * for smaller or shorter-K products, or when no rule fills the device, the
+ * nearest rule.
  * Split-K tiles add partial sums with atomics, so their last bits may differ
  * from run to run (within the accuracy bound).  The split decision and the
  * fill check need the device's compute units and occupancy; without a device
