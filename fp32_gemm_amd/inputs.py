@@ -55,8 +55,9 @@ WORKLOADS = {
 
 # Extra aligned shapes the autotuner records rules for: between the graded
 # workloads, where no graded rule's tile fills the device's resident slots,
-# two skinny products and two short-K products (bound by reading and writing
-# C); none is graded, and the tuner's exact check plus a sampled GPU test are
+# two skinny products, two short-K products (bound by reading and writing
+# C) and one deep-K product (few tiles, so every tile is split); none is
+# graded, and the tuner's exact check plus a sampled GPU test are
 # their parity bar.
 TUNING_EXTRA = {
     w.name: w
@@ -69,6 +70,7 @@ TUNING_EXTRA = {
         Workload("skinny8192x64x8192", 8192, 64, 8192, "uniform", "uniform", 0.5, 3.0, 14),
         Workload("shortk4096x4096x16", 4096, 4096, 16, "uniform", "uniform", 0.5, 3.0, 15),
         Workload("shortk8192x8192x32", 8192, 8192, 32, "uniform", "uniform", 0.5, 3.0, 16),
+        Workload("deepk1024x1024x65536", 1024, 1024, 65536, "uniform", "uniform", 0.5, 3.0, 17),
     ]
 }
 
