@@ -45,17 +45,25 @@ def _time(fn, warm, reps, stream):
     return float(np.median(per)), float(per.min()), float(per.max())
 
 
-def _exact_check(cfg_id, M, N, K, dev, samples=1500):
-    """Integer-valued inputs: sampled outputs must equal int64 arithmetic."""
+def _exact_inputs(M, N, K, dev, samples=1500):
+    """Integer-valued inputs on the device and the expected sampled outputs
+    from int64 arithmetic; drawn once per shape and shared by every
+    configuration's check."""
     A, B, C = inputs.make_small_int(M, N, K, seed=4242)
-    Ad, Bd = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
-    Cd = torch.from_numpy(C).to(dev)
-    fg.sgemm_ex(Ad, Bd, Cd, 0.5, 3.0, cfg_id=cfg_id)
-    torch.cuda.synchronize()
     rows, cols = inputs.sample_indices(M, N, samples, seed=4243)
-    got = Cd.cpu().numpy()[rows, cols]
     s = np.einsum("ij,ji->i", A[rows].astype(np.int64), B[:, cols].astype(np.int64))
     want = (0.5 * s + 3.0 * C[rows, cols].astype(np.float64)).astype(np.float32)
+    dev_in = tuple(torch.from_numpy(x).to(dev) for x in (A, B, C))
+    return dev_in, torch.from_numpy(rows).to(dev), torch.from_numpy(cols).to(dev), want
+
+
+def _exact_check(cfg_id, chk):
+    """Sampled outputs of one configuration on the shared integer inputs must
+    equal the int64 result bit for bit."""
+    (Ad, Bd, C0), rows, cols, want = chk
+    Cd = C0.clone()
+    fg.sgemm_ex(Ad, Bd, Cd, 0.5, 3.0, cfg_id=cfg_id)
+    got = Cd[rows, cols].cpu().numpy()
     return bool(np.array_equal(got.view(np.uint32), want.view(np.uint32)))
 
 
@@ -77,8 +85,9 @@ def tune_shape(w, dev, configs, log, finalists=6):
     stream = torch.cuda.current_stream(dev)
     flops = model.flops(w.M, w.N, w.K)
     results = []
+    chk = _exact_inputs(w.M, w.N, w.K, dev)
     for c in configs:
-        ok = _exact_check(c["id"], w.M, w.N, w.K, dev)
+        ok = _exact_check(c["id"], chk)
         rec = {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "cfg_id": c["id"],
                "tuple": list(c["tuple"]), "path": c["path_name"], "exact": ok}
         if ok:
