@@ -57,31 +57,37 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_each_way": 4 * n, "launches": 3}), flush=True)
 
 
-def cpu_baseline(w, A, B, C, target_s):
-    """The oracle, as it stands, on the first R rows of the same workload."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            return next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        return "unknown"
+
+
+def oracle_product(w, A, B, C, target_s):
+    """The oracle, as it stands, on the whole product of the same workload:
+    one pass gives the fp64 result every GPU output is checked against; more
+    passes of the same call (when target_s > 0) bring the CPU sample to about
+    target_s seconds for the reported baseline.  Returns (C64, baseline)."""
     from oracle import oracle
     oracle.build(force=False)
     threads = oracle.max_threads()
-    rows = 8
     t0 = time.perf_counter()
-    oracle.sgemm(A[:rows], B, C[:rows], w.alpha, w.beta)
-    probe = time.perf_counter() - t0
-    rows = int(max(8, min(w.M, rows * max(1.0, (target_s - probe) / max(probe, 1e-3)))))
-    t0 = time.perf_counter()
-    oracle.sgemm(A[:rows], B, C[:rows], w.alpha, w.beta)
+    _, C64 = oracle.sgemm(A, B, C, w.alpha, w.beta)
     dt = time.perf_counter() - t0
-    # Where the whole product takes well under the target, repeat it (the
-    # same call on the same inputs) until about the target has been spent.
     passes = 1
-    while rows == w.M and dt < 0.9 * target_s and dt / passes < target_s:
+    while target_s > 0 and dt < 0.9 * target_s and dt / passes < target_s:
         oracle.sgemm(A, B, C, w.alpha, w.beta)
         passes += 1
         dt = time.perf_counter() - t0
-    gflops = 2.0 * rows * w.N * w.K * passes / dt / 1e9
-    what = (f"first {rows} of {w.M} rows of the same {w.M}x{w.N}x{w.K} product" if rows < w.M
-            else f"the whole {w.M}x{w.N}x{w.K} product, {passes} pass{'es' if passes > 1 else ''}")
-    return {"value": round(gflops, 3), "unit": "GFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{what} (fp64 accumulation, OpenMP over rows), {dt:.1f} s"}
+    gflops = 2.0 * w.M * w.N * w.K * passes / dt / 1e9
+    base = {"value": round(gflops, 3), "unit": "GFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"the whole {w.M}x{w.N}x{w.K} product, {passes} pass"
+                      f"{'es' if passes > 1 else ''} (fp64 accumulation, OpenMP over rows), "
+                      f"{dt:.1f} s; the first pass is also the parity reference"}
+    return C64, base
 
 
 def oracle_timing(inputs, model, max_seconds=20.0):
@@ -91,12 +97,7 @@ def oracle_timing(inputs, model, max_seconds=20.0):
     from oracle import oracle
     oracle.build(force=False)
     threads = oracle.max_threads()
-    model_name = "unknown"
-    try:
-        with open("/proc/cpuinfo") as f:
-            model_name = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
-    except (OSError, StopIteration):
-        pass
+    model_name = cpu_model()
     out = []
 
     def run(w, A, B, C, nthreads):
@@ -158,6 +159,21 @@ def ladder(fg, inputs, model, w, dev, args):
                               "pct_of_peak": round(100 * flops / (ms * 1e-3) / 1e12
                                                    / model.PEAK_FP32_TFLOPS, 2)})
     print(json.dumps(out), flush=True)
+
+
+def kernel_resources(fg, info, plan, dev):
+    """Registers, scratch, LDS and residency of the kernel the launch ran."""
+    import torch
+    vec = bool(plan["vector_variant"])
+    attr = fg.kernel_attributes(info["id"], vec)
+    rep = next((c for c in fg.configs() if c["id"] == info["id"]), {})
+    res = rep.get("resources_vec" if vec else "resources_scalar") or {}
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    return {"vgprs": res.get("VGPRs"), "agprs": res.get("AGPRs"),
+            "sgprs": res.get("TotalSGPRs"), "scratch_bytes_per_lane": attr["scratch_bytes"],
+            "lds_bytes": attr["lds_bytes"], "waves_per_simd": res.get("Occupancy"),
+            "workgroups_per_cu": plan["slots"] // cus if plan["slots"] else None,
+            "compute_units": cus, "threads_per_workgroup": info["NT"]}
 
 
 def main():
@@ -234,12 +250,7 @@ def main():
     per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])  # ms
     avg_ms = float(ev[0].elapsed_time(ev[-1])) / args.steps
 
-    # Parity of the last timed output against the oracle on sampled entries.
-    from oracle import oracle
     last = Cs[(total - 1) % pool].cpu().numpy()
-    rows, cols = inputs.sample_indices(w.M, w.N, 2000, seed=w.seed + 100)
-    _, e64 = oracle.entries(rows, cols, A, B, C, w.alpha, w.beta)
-    parity = oracle.rel_error(last[rows, cols], e64, w.K, np.abs(A).max(), np.abs(B).max())
 
     flops = model.flops(w.M, w.N, w.K)
     value = flops * args.steps / wall / 1e9
@@ -285,62 +296,82 @@ def main():
         },
         "timing_ms": {"event_avg": round(avg_ms, 4), "median": round(float(np.median(per)), 4),
                       "min": round(float(per.min()), 4), "max": round(float(per.max()), 4),
-                      "spread": round(float((per.max() - per.min()) / np.median(per)), 4)},
-        "parity_err": parity,
+                      "spread": round(float((per.max() - per.min()) / np.median(per)), 4),
+                      "per_launch": [round(float(x), 4) for x in per]},
+        "kernel": kernel_resources(fg, info, plan, dev),
     }
     if not args.no_context:
-        # The same warm-up and launch count as the timed kernel above, so the
-        # vendor library is compared at its steady clock too.  torch.mm is
-        # the plain product (no alpha, no beta read of C).
+        # Warm caches: the two libraries alternate in batches of five
+        # launches (eight batches each, after a warm-up of each), so clock
+        # and temperature drift affect them alike.  torch.mm is the plain
+        # product (no alpha, no beta read of C).
         Cm = torch.empty_like(C0)
-        mm_warm, mm_reps = max(args.warmup, 10), max(args.steps, 20)
-        for _ in range(mm_warm):
-            torch.mm(Ad, Bd, out=Cm)
-        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(mm_reps):
-            torch.mm(Ad, Bd, out=Cm)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        mm = flops / (e0.elapsed_time(e1) / mm_reps * 1e-3) / 1e12
+        ours = lambda Cx: fg.sgemm_ex(Ad, Bd, Cx, w.alpha, w.beta, stream=stream, cfg_id=args.cfg)
+        vendor = lambda Cx: torch.mm(Ad, Bd, out=Cx)
+        mm_warm, batches, batch = 10, 8, 5
+        for _ in range(mm_warm):
+            vendor(Cm)
+        warm, warm_mm = [], []
+        use = 0
+        for _ in range(batches):
+            for f, acc in ((ours, warm), (vendor, warm_mm)):
+                torch.cuda.synchronize()
+                e0.record(stream)
+                for _ in range(batch):
+                    f(Cs[use % pool] if f is ours else Cm)
+                    use += 1
+                e1.record(stream)
+                torch.cuda.synchronize()
+                acc.append(e0.elapsed_time(e1) / batch)
+        warm_ms, mm_ms = float(np.median(warm)), float(np.median(warm_mm))
+        mm = flops / (mm_ms * 1e-3) / 1e12
         # Cold caches: a 512 MiB write between launches evicts A, B and C
         # from the L2s and the 256 MiB Infinity Cache; each launch is timed
         # alone, on a pristine C written before the eviction.  Three untimed
-        # launches before each eviction hold the clock: isolated launches
-        # after a synchronisation otherwise start ~25 % slower and take about
-        # thirty launches to recover, whatever the caches hold.
+        # launches before each eviction hold the clock (isolated launches
+        # after a synchronisation otherwise start slower), and the two
+        # libraries alternate launch by launch, so a clock still settling
+        # favours neither.
         scratch = torch.empty(128 << 20, dtype=torch.float32, device=dev)
         spare = torch.empty_like(C0)
 
-        def cold_times(f):
-            t = []
-            for i in range(10):
-                Cs[i % pool].copy_(C0)
-                for _ in range(3):
-                    f(spare)
-                scratch.fill_(float(i))
-                e0.record(stream)
-                f(Cs[i % pool])
-                e1.record(stream)
-                torch.cuda.synchronize()
-                t.append(e0.elapsed_time(e1))
-            return float(np.median(t))
+        def cold_once(f, i):
+            Cs[i % pool].copy_(C0)
+            for _ in range(3):
+                f(spare)
+            scratch.fill_(float(i))
+            e0.record(stream)
+            f(Cs[i % pool])
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1)
 
-        cold_ms = cold_times(lambda Cx: fg.sgemm_ex(Ad, Bd, Cx, w.alpha, w.beta, stream=stream,
-                                                    cfg_id=args.cfg))
-        cold_mm_ms = cold_times(lambda Cx: torch.mm(Ad, Bd, out=Cx))
+        cold, cold_mm = [], []
+        for i in range(10):
+            cold.append(cold_once(ours, i))
+            cold_mm.append(cold_once(vendor, i))
+        cold_ms, cold_mm_ms = float(np.median(cold)), float(np.median(cold_mm))
         del scratch, spare
-        out["context"] = {"torch_mm_tflops": round(mm, 2),
-                          "this_vs_torch_mm": round(achieved / mm, 3),
-                          "torch_mm_launches": {"warmup": mm_warm, "timed": mm_reps},
+        out["context"] = {"interleaved_tflops": round(flops / (warm_ms * 1e-3) / 1e12, 2),
+                          "torch_mm_tflops": round(mm, 2),
+                          "this_vs_torch_mm": round(mm_ms / warm_ms, 3),
+                          "interleaved_launches": {"torch_mm_warmup": mm_warm, "batches": batches,
+                                                   "per_batch": batch},
                           "cold_cache_tflops": round(flops / (cold_ms * 1e-3) / 1e12, 2),
                           "cold_cache_ms_median": round(cold_ms, 4),
                           "torch_mm_cold_cache_tflops": round(flops / (cold_mm_ms * 1e-3) / 1e12, 2),
+                          "cold_cache_this_vs_torch_mm": round(cold_mm_ms / cold_ms, 3),
                           "note": "vendor BLAS timing (plain A*B), context only; never used for "
                                   "dispatch or parity"}
+    # Parity: every output of the last timed launch against the oracle's
+    # whole product (the first pass of the CPU baseline's sample).
+    from oracle import oracle
+    C64, base = oracle_product(w, A, B, C, 0.0 if args.no_cpu_baseline else args.cpu_seconds)
+    out["parity_err"] = oracle.rel_error(last, C64, w.K, np.abs(A).max(), np.abs(B).max())
+    out["parity_outputs"] = f"all {w.M * w.N} outputs of the last timed launch"
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, A, B, C, args.cpu_seconds)
+        out["cpu_baseline"] = base
     print(json.dumps(out), flush=True)
 
 

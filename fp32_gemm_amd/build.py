@@ -18,6 +18,7 @@ import re
 import shutil
 import subprocess
 import sys
+import zlib
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
@@ -37,8 +38,51 @@ HIP_FLAGS = [
 VALU, MFMA32, MFMA16 = 0, 1, 2
 
 
-def candidates():
+# Tuples whose kernel (in either variant) the compiler had to spill to
+# scratch memory: written by build() from the compiler's resource report and
+# left out of the compiled table, so no configuration a caller can select
+# spills.  A build that finds a new spilling tuple adds it here and compiles
+# the affected units again.
+SPILLING = os.path.join(PKG, "spilling_tuples.json")
+
+
+def _spilling():
+    if not os.path.exists(SPILLING):
+        return set()
+    with open(SPILLING) as f:
+        return {tuple(t) for t in json.load(f)["tuples"]}
+
+
+def valu_grid():
+    """The VALU sweep grid: BM, BN in {64, 128, 256}, BK in {8, 16, 32}, WM, WN
+    in {32 .. 256}, WNITER in {1, 2, 4}, TM, TN in {4, 8}, 128, 256 or 512
+    threads, and 32 to 128 accumulators per lane (32-bank swizzle, no
+    schedule options).  Only the cheap necessary conditions are applied here
+    (warp tiles inside the block, one wave per warp tile); the C++ checker
+    decides legality when the instance units compile."""
+    import itertools
+    out = []
+    for BM, BN, BK, WM, WN, WNITER, TM, TN, NT in itertools.product(
+            (64, 128, 256), (64, 128, 256), (8, 16, 32), (32, 64, 128, 256), (32, 64, 128, 256),
+            (1, 2, 4), (4, 8), (4, 8), (128, 256, 512)):
+        if WM > BM or WN > BN or (BM // WM) * (BN // WN) * 64 != NT:
+            continue
+        if not 32 <= WM * WN // 64 <= 128:
+            continue
+        out.append((BM, BN, BK, WM, WN, WNITER, TM, TN, NT, VALU, 32, 0))
+    return out
+
+
+def candidates(include_spilling=False):
     """Candidate tuples (BM, BN, BK, WM, WN, WNITER, TM, TN, NT, path, swz, opt)."""
+    out = _all_candidates()
+    if include_spilling:
+        return out
+    bad = _spilling()
+    return [t for t in out if t not in bad]
+
+
+def _all_candidates():
     out = []
     # MFMA 32x32x2: every block/warp tile split into 1, 2, 4 or 8 waves.
     for BM, BN in [(256, 256), (256, 128), (128, 256), (128, 128), (128, 64), (64, 128), (64, 64)]:
@@ -217,6 +261,7 @@ def candidates():
             out.append(base + (swz, 0))
             if base[9] != VALU:
                 out.append(base + (swz, 3))
+    out += valu_grid()
     seen, uniq = set(), []
     for t in out:
         if t not in seen:
@@ -234,11 +279,14 @@ def _write_if_changed(path, text):
         f.write(text)
 
 
-def generate(n_units=16):
+def generate(n_units=24):
     os.makedirs(BUILD, exist_ok=True)
     cands = candidates()
-    units = [cands[i::n_units] for i in range(n_units)]
-    units = [u for u in units if u]
+    # Each tuple's unit is a hash of the tuple, so dropping one tuple changes
+    # only its own unit.
+    units = [[] for _ in range(n_units)]
+    for t in cands:
+        units[zlib.crc32(repr(t).encode()) % n_units].append(t)
     srcs = []
     for ui, unit in enumerate(units):
         lines = ['#include "registry.hpp"', "namespace fp32gemm {",
@@ -283,8 +331,33 @@ def _compile(src, obj, remarks):
     return res
 
 
+_TILE_NAME = re.compile(r"TileCfgILi" + r"ELi".join([r"(\d+)"] * 12) + r"EEELb(\d)")
+
+
 def build(verbose=True, jobs=None):
-    """Compile every HIP source for gfx950 and link the shared library."""
+    """Compile every HIP source for gfx950 and link the shared library.  If a
+    tuple's kernel spills, it is recorded in spilling_tuples.json and the
+    units are compiled again without it."""
+    for attempt in range(3):
+        resources = _build_once(verbose, jobs)
+        new = set()
+        for name, v in resources.items():
+            m = _TILE_NAME.search(name)
+            if m and v.get("ScratchSize", 0) > 0:
+                new.add(tuple(int(x) for x in m.groups()[:12]))
+        if not new:
+            return LIB
+        bad = sorted(_spilling() | new)
+        with open(SPILLING, "w") as f:
+            json.dump({"note": "tuples whose kernel spilled to scratch in the compiler's resource "
+                               "report; left out of the compiled table",
+                       "tuples": [list(t) for t in bad]}, f, indent=0)
+        if verbose:
+            print(f"[build] {len(new)} spilling tuples excluded; compiling again", flush=True)
+    raise RuntimeError("build: spilling tuples remain after three passes")
+
+
+def _build_once(verbose, jobs):
     t_srcs = generate()
     jobs = jobs or min(16, os.cpu_count() or 4)
     api = os.path.join(CSRC, "sgemm_api.hip")
@@ -309,7 +382,7 @@ def build(verbose=True, jobs=None):
     spills = {k: v for k, v in resources.items() if v.get("ScratchSize", 0) > 0}
     if verbose:
         print(f"[build] {LIB}: {len(resources)} kernels, {len(spills)} with scratch", flush=True)
-    return LIB
+    return resources
 
 
 def clean():

@@ -59,7 +59,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // Buffer resources never describe more than kMaxRecords bytes; a masked
 // element is loaded from kMaskedOffset, which is therefore always out of
 // range and reads as zero.
-constexpr long long kMaxRecords = 0x7FFFFFF0LL;
+constexpr long long kMaxRecords = kMaxBufferBytes;
 constexpr int kMaskedOffset = 0x7FFFFFF0;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const float* base, long long bytes) {

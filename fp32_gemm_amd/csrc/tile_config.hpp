@@ -101,6 +101,19 @@ constexpr int dma_ops_per_slice(const Tile& t, int fpl) {
   return (t.BM * t.BK + t.BK * t.BN) / (fpl * t.NT);
 }
 
+// Addressing limits.  The kernels form 64-bit tile base addresses but
+// in-tile byte offsets in 32 bits: a row index below the block tile height
+// (or BK, for B) times a leading dimension, times 4.  Every such offset must
+// stay inside one buffer resource, whose record count is at most
+// kMaxBufferBytes; the largest accepted leading dimension and the tallest
+// block tile are sized together so that it does.
+constexpr long long kMaxBufferBytes = 0x7FFFFFF0LL;
+constexpr long long kMaxLeadingDim = (1LL << 21) - 1;
+constexpr int kMaxTileRows = 256;
+static_assert(kMaxTileRows * kMaxLeadingDim * 4 <= kMaxBufferBytes,
+              "in-tile offsets of the tallest tile at the largest leading dimension overflow a "
+              "buffer resource");
+
 // Machine limits the checker enforces.
 struct Target {
   int wave;           // lanes per wave (warp)
@@ -124,7 +137,8 @@ constexpr Target kPageModel{32, 48 * 1024, 1, 128, 1 << 30, 1 << 30, false, fals
 // Reason codes, one per guard, in evaluation order.
 enum Reason : int {
   kLegal = 0,
-  kBadRange = 1,            // a parameter is non-positive, or too many threads
+  kBadRange = 1,            // a parameter is non-positive, too many threads, or BM or
+                            // BK above kMaxTileRows
   kThreadsNotWaves = 2,     // NT is not a whole number of waves
   kBlockNotWarpTiled = 3,   // BM % WM or BN % WN
   kWarpCount = 4,           // warp tiles != waves
@@ -201,7 +215,8 @@ constexpr int vgpr_estimate(const Tile& t, int wave) {
 
 constexpr int check_tile(const Tile& t, const Target& m) {
   if (t.BM <= 0 || t.BN <= 0 || t.BK <= 0 || t.WM <= 0 || t.WN <= 0 || t.WNITER <= 0 ||
-      t.TM <= 0 || t.TN <= 0 || t.NT <= 0 || t.NT > 1024)
+      t.TM <= 0 || t.TN <= 0 || t.NT <= 0 || t.NT > 1024 || t.BM > kMaxTileRows ||
+      t.BK > kMaxTileRows)
     return kBadRange;
   if (t.path != kPathValu && !m.allow_mfma) return kNoMfmaOnTarget;
   if ((t.opt & ~kOptAll) != 0) return kBadOptions;

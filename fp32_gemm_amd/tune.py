@@ -78,7 +78,10 @@ def usable_configs(vector_variant=True):
     return out
 
 
-def tune_shape(w, dev, configs, log, finalists=6):
+def tune_shape(w, dev, configs, log, finalists=6, progress=None):
+    """Sweep one shape: exact check and short timing of every configuration,
+    then the `finalists` fastest of each path re-timed interleaved with the
+    long protocol.  Returns (best overall, best per path, all records)."""
     A, B, C = inputs.make(w)
     Ad, Bd = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
     Cd = torch.from_numpy(C).to(dev)
@@ -86,7 +89,8 @@ def tune_shape(w, dev, configs, log, finalists=6):
     flops = model.flops(w.M, w.N, w.K)
     results = []
     chk = _exact_inputs(w.M, w.N, w.K, dev)
-    for c in configs:
+    t0 = time.time()
+    for i, c in enumerate(configs):
         ok = _exact_check(c["id"], chk)
         rec = {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "cfg_id": c["id"],
                "tuple": list(c["tuple"]), "path": c["path_name"], "exact": ok}
@@ -97,7 +101,12 @@ def tune_shape(w, dev, configs, log, finalists=6):
                        protocol="short")
         results.append(rec)
         log(rec)
-    ok = sorted((r for r in results if r["exact"]), key=lambda r: r["ms"])[:finalists]
+        if progress and (i + 1) % 50 == 0:
+            progress(f"[tune] {w.name}: {i + 1}/{len(configs)} swept ({time.time() - t0:.0f} s)")
+    by_path = {}
+    for r in sorted((r for r in results if r["exact"]), key=lambda r: r["ms"]):
+        by_path.setdefault(r["path"], []).append(r)
+    ok = [r for rs in by_path.values() for r in rs[:finalists]]
     # Finalists are timed interleaved (one batch of each in turn, repeated),
     # so clock and temperature drift affect them alike.
     warm, reps = LONG
@@ -123,8 +132,35 @@ def tune_shape(w, dev, configs, log, finalists=6):
                    tflops=flops / (med * 1e-3) / 1e12, protocol="long")
         results.append(fin)
         log(fin)
-    best = min((r for r in results if r.get("protocol") == "long"), key=lambda r: r["ms"])
-    return best, results
+    longs = [r for r in results if r.get("protocol") == "long"]
+    best_by_path = {}
+    for r in longs:
+        if r["path"] not in best_by_path or r["ms"] < best_by_path[r["path"]]["ms"]:
+            best_by_path[r["path"]] = r
+    for path, b in best_by_path.items():
+        b["swept"] = sum(1 for r in results if r.get("protocol") == "short" and r["path"] == path)
+        b["failed_exact"] = sum(1 for r in results if not r["exact"] and r["path"] == path)
+    best = min(longs, key=lambda r: r["ms"])
+    return best, best_by_path, results
+
+
+def write_summary(best_by_shape_path, path, command):
+    """Markdown table of the best tuple per (shape, path)."""
+    lines = ["# Autotuner winners per (shape, path)", "",
+             f"Command: `{command}`", "",
+             "Every compiled, non-spilling configuration of each path was checked exactly on "
+             "integer-valued inputs and timed with the short protocol (3 warm-up, 10 timed "
+             "launches); the six fastest of each path were then re-timed interleaved (20 "
+             "warm-up, 12 batches of 5). Times are the long protocol's median.", "",
+             "| shape | path | swept | best tuple (BM,BN,BK,WM,WN,WNITER,TM,TN,NT,path,swz,opt) "
+             "| ms | TFLOP/s | % of 157.3 |",
+             "|---|---|---|---|---|---|---|"]
+    for (shape, pth), b in best_by_shape_path.items():
+        lines.append(f"| {shape} {b['M']}x{b['N']}x{b['K']} | {pth} | {b['swept']} | "
+                     f"{','.join(str(x) for x in b['tuple'])} | {b['ms']:.4f} | "
+                     f"{b['tflops']:.1f} | {100 * b['tflops'] / model.PEAK_FP32_TFLOPS:.1f} |")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
 
 
 def write_table(best_by_shape, path, defaults):
@@ -158,19 +194,23 @@ def main():
     ap.add_argument("--out", default="tune_results.jsonl")
     ap.add_argument("--table-out", default=None)
     ap.add_argument("--paths", default="valu,mfma32,mfma16")
-    ap.add_argument("--prune-above", type=float, default=2 * 4096 ** 3 * 1.5,
-                    help="shapes with more FLOP than this only try the best --keep configs "
-                         "of the largest shape already swept")
+    ap.add_argument("--prune-above", type=float, default=float("inf"),
+                    help="shapes with more FLOP than this only try the best --keep configs per "
+                         "path of the --prune-from shape's short sweep (default: no pruning)")
+    ap.add_argument("--prune-from", default="sq4096",
+                    help="the shape whose ranking prunes larger shapes (swept first)")
     ap.add_argument("--keep", type=int, default=32)
+    ap.add_argument("--summary-out", default=None,
+                    help="write a markdown table of the best tuple per (shape, path)")
     ap.add_argument("--top-from", default=None,
                     help="only try tuples ranked in the top --top of a previous results file "
                          "(per workload, short protocol)")
     ap.add_argument("--top", type=int, default=24)
     ap.add_argument("--filter", default=None,
                     help="Python expression over a config dict c (e.g. \"c['BK'] == 32\")")
-    ap.add_argument("--finalists", type=int, default=10,
-                    help="tuples re-timed interleaved with the long protocol; the sweep's "
-                         "short timings are noisier than the gaps between the best tuples")
+    ap.add_argument("--finalists", type=int, default=6,
+                    help="tuples per path re-timed interleaved with the long protocol; the "
+                         "sweep's short timings are noisier than the gaps between the best tuples")
     ap.add_argument("--best", default=None,
                     help="print the best tuple recorded for this workload in --out and exit")
     args = ap.parse_args()
@@ -205,27 +245,42 @@ def main():
         if rec.get("protocol") == "long" or not rec["exact"]:
             print(json.dumps(rec), flush=True)
 
-    bests = []
-    ranked = None  # configs of the largest shape swept so far, fastest first
+    bests, per_path = [], {}
+    ranked = None  # the --prune-from shape's configurations, fastest first per path
     shapes = {**inputs.WORKLOADS, **inputs.TUNING_EXTRA}
-    names = sorted(args.workloads.split(","), key=lambda n: model.flops(
-        shapes[n].M, shapes[n].N, shapes[n].K))
+    names = sorted(args.workloads.split(","), key=lambda n: (n != args.prune_from, model.flops(
+        shapes[n].M, shapes[n].N, shapes[n].K)))
+    progress = lambda msg: print(msg, flush=True)
     for name in names:
         w = shapes[name]
         t0 = time.time()
         use = configs[w.K % 4 == 0 and w.N % 4 == 0]
-        if ranked is not None and model.flops(w.M, w.N, w.K) > args.prune_above:
-            use = ranked[:args.keep]
+        if model.flops(w.M, w.N, w.K) > args.prune_above:
+            if ranked is None:
+                raise SystemExit(f"tune: pruning {name} needs --prune-from {args.prune_from} "
+                                 f"in --workloads")
+            ids = {c["id"] for c in use}
+            use = [c for pth in ranked for c in ranked[pth][:args.keep] if c["id"] in ids]
         print(f"[tune] {name}: {len(use)} configs", flush=True)
-        best, results = tune_shape(w, dev, use, log, finalists=args.finalists)
-        if model.flops(w.M, w.N, w.K) <= args.prune_above:
+        best, best_path, results = tune_shape(w, dev, use, log, finalists=args.finalists,
+                                              progress=progress)
+        if name == args.prune_from:
             order = sorted((r for r in results if r.get("protocol") == "short" and r["exact"]),
                            key=lambda r: r["ms"])
             by_id = {c["id"]: c for c in configs[True] + configs[False]}
-            ranked = [by_id[r["cfg_id"]] for r in order]
+            ranked = {}
+            for r in order:
+                ranked.setdefault(r["path"], []).append(by_id[r["cfg_id"]])
+        for pth, b in best_path.items():
+            per_path[(name, pth)] = b
+            print(f"[tune] {name} {pth}: best cfg {b['cfg_id']} {b['tuple']} {b['ms']:.4f} ms "
+                  f"{b['tflops']:.1f} TFLOP/s of {b['swept']} swept", flush=True)
         print(f"[tune] {name}: best cfg {best['cfg_id']} {best['tuple']} {best['ms']:.4f} ms "
               f"{best['tflops']:.1f} TFLOP/s ({time.time() - t0:.0f} s)", flush=True)
         bests.append(best)
+    if args.summary_out:
+        write_summary(per_path, args.summary_out, "python -m fp32_gemm_amd.tune " +
+                      " ".join(sys.argv[1:]))
     if args.table_out:
         by = {b["workload"]: b["tuple"] for b in bests}
         large = by.get("sq4096", bests[0]["tuple"])

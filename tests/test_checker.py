@@ -82,6 +82,16 @@ def test_each_guard_trips(reason, tup):
     assert fg.check_tuple(tup, "gfx950") == reason
 
 
+def test_tile_height_limit():
+    # In-tile offsets are 32-bit: a block tile taller than 256 rows at the
+    # largest leading dimension (2^21 - 1) would leave a buffer resource's
+    # range, so the range guard rejects it although every other guard holds.
+    tall = (512, 64, 16, 128, 64, 1, 4, 4, 256, VALU, 0)
+    assert fg.check_tuple(tall, "gfx950") == 1
+    assert fg.check_tuple((256, 64, 16, 128, 64, 1, 4, 4, 128, VALU, 0), "gfx950") != 1
+    assert 256 * ((1 << 21) - 1) * 4 <= 0x7FFFFFF0 < 512 * ((1 << 21) - 1) * 4
+
+
 def test_lane_count_and_ownership_guards_are_implied():
     """Guards 8 (lanes per sub-tile) and 12 (single ownership) cannot trip
     first: once WMITER divides exactly (guards 5-7), the lanes per sub-tile
