@@ -165,7 +165,7 @@ def kernel_resources(fg, info, plan, dev):
     """Registers, scratch, LDS and residency of the kernel the launch ran."""
     import torch
     vec = bool(plan["vector_variant"])
-    attr = fg.kernel_attributes(info["id"], vec)
+    attr = fg.binding.kernel_attributes(info["id"], vec)
     rep = next((c for c in fg.configs() if c["id"] == info["id"]), {})
     res = rep.get("resources_vec" if vec else "resources_scalar") or {}
     cus = torch.cuda.get_device_properties(dev).multi_processor_count

@@ -144,13 +144,13 @@ def tune_shape(w, dev, configs, log, finalists=6, progress=None):
     return best, best_by_path, results
 
 
-def write_summary(best_by_shape_path, path, command):
+def write_summary(best_by_shape_path, path, command, finalists=6):
     """Markdown table of the best tuple per (shape, path)."""
     lines = ["# Autotuner winners per (shape, path)", "",
              f"Command: `{command}`", "",
-             "Every compiled, non-spilling configuration of each path was checked exactly on "
-             "integer-valued inputs and timed with the short protocol (3 warm-up, 10 timed "
-             "launches); the six fastest of each path were then re-timed interleaved (20 "
+             f"Every compiled, non-spilling configuration of each path was checked exactly on "
+             f"integer-valued inputs and timed with the short protocol (3 warm-up, 10 timed "
+             "launches); the {finalists} fastest of each path were then re-timed interleaved (20 "
              "warm-up, 12 batches of 5). Times are the long protocol's median.", "",
              "| shape | path | swept | best tuple (BM,BN,BK,WM,WN,WNITER,TM,TN,NT,path,swz,opt) "
              "| ms | TFLOP/s | % of 157.3 |",
@@ -280,7 +280,7 @@ def main():
         bests.append(best)
     if args.summary_out:
         write_summary(per_path, args.summary_out, "python -m fp32_gemm_amd.tune " +
-                      " ".join(sys.argv[1:]))
+                      " ".join(sys.argv[1:]), args.finalists)
     if args.table_out:
         by = {b["workload"]: b["tuple"] for b in bests}
         large = by.get("sq4096", bests[0]["tuple"])
