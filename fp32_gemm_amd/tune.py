@@ -148,9 +148,9 @@ def write_summary(best_by_shape_path, path, command, finalists=6):
     """Markdown table of the best tuple per (shape, path)."""
     lines = ["# Autotuner winners per (shape, path)", "",
              f"Command: `{command}`", "",
-             f"Every compiled, non-spilling configuration of each path was checked exactly on "
-             f"integer-valued inputs and timed with the short protocol (3 warm-up, 10 timed "
-             "launches); the {finalists} fastest of each path were then re-timed interleaved (20 "
+             "Every compiled, non-spilling configuration of each path was checked exactly on "
+             "integer-valued inputs and timed with the short protocol (3 warm-up, 10 timed "
+             f"launches); the {finalists} fastest of each path were then re-timed interleaved (20 "
              "warm-up, 12 batches of 5). Times are the long protocol's median.", "",
              "| shape | path | swept | best tuple (BM,BN,BK,WM,WN,WNITER,TM,TN,NT,path,swz,opt) "
              "| ms | TFLOP/s | % of 157.3 |",
