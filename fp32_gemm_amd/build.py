@@ -261,6 +261,20 @@ def _all_candidates():
             out.append(base + (swz, 0))
             if base[9] != VALU:
                 out.append(base + (swz, 3))
+    # K-sliced workgroups (opt bit 9): two wave groups split the K slices of
+    # one tile, for shapes with about one tile per compute unit.
+    KS = 512
+    for base in [(64, 64, 64, 32, 32, 1, 16, 1, 512, MFMA32, 32),
+                 (64, 64, 32, 32, 32, 1, 16, 1, 512, MFMA32, 32),
+                 (64, 64, 16, 32, 32, 1, 16, 1, 512, MFMA32, 32),
+                 (64, 64, 64, 32, 32, 2, 4, 1, 512, MFMA16, 32),
+                 (64, 64, 32, 32, 32, 2, 4, 1, 512, MFMA16, 32),
+                 (128, 64, 32, 64, 32, 1, 16, 1, 512, MFMA32, 32),
+                 (64, 128, 32, 32, 64, 2, 16, 1, 512, MFMA32, 32),
+                 (128, 128, 32, 64, 64, 2, 16, 1, 512, MFMA32, 32),
+                 (128, 128, 32, 64, 64, 4, 4, 1, 512, MFMA16, 32),
+                 (128, 128, 32, 64, 32, 2, 4, 1, 1024, MFMA16, 64)]:
+        out += [base + (opt | KS,) for opt in (16, 17, 18, 19)]
     out += valu_grid()
     seen, uniq = set(), []
     for t in out:

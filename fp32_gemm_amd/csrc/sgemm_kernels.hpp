@@ -577,7 +577,7 @@ __device__ __forceinline__ void k_loop_pipelined(const KernelArgs& p, float* lds
 // MFMA block, or one row of VALU patches) issues all its loads of C before its
 // stores, so a wave waits for memory once per chunk rather than once per
 // element.
-template <class Cfg, bool VEC>
+template <class Cfg, bool VEC, class OccCfg = Cfg>
 __device__ __forceinline__ void epilogue(float* cw, int ldc, int rlim, int clim, int lane,
                                          float alpha, float beta, const Acc<Cfg>& acc) {
   constexpr Geom g = make_geom(Cfg::tile);
@@ -640,9 +640,10 @@ __device__ __forceinline__ void epilogue(float* cw, int ldc, int rlim, int clim,
     // a time: the larger chunk spills there, or costs the occupancy.
     constexpr int blk = mfma_blk(g), regs = mfma_regs(g);
     constexpr int kBlocks = g.WMITER * g.WNITER;
-    constexpr int kLdsBlocks = kGfx950.lds_bytes / lds_bytes(Cfg::tile, kGfx950);
-    constexpr int kBlocksPerCu = min_blocks_of(Cfg::tile) > kLdsBlocks ? min_blocks_of(Cfg::tile) : kLdsBlocks;
-    constexpr int kWavesPerSimd = (Cfg::NT + 255) / 256 * (kBlocksPerCu > 1 ? kBlocksPerCu : 1);
+    // (OccCfg: the launched tuple, whose threads and LDS set the residency.)
+    constexpr int kLdsBlocks = kGfx950.lds_bytes / lds_bytes(OccCfg::tile, kGfx950);
+    constexpr int kBlocksPerCu = min_blocks_of(OccCfg::tile) > kLdsBlocks ? min_blocks_of(OccCfg::tile) : kLdsBlocks;
+    constexpr int kWavesPerSimd = (OccCfg::NT + 255) / 256 * (kBlocksPerCu > 1 ? kBlocksPerCu : 1);
     constexpr int kValues = kWavesPerSimd >= 3 ? regs : 32;
     constexpr int kChunk = (kValues / regs) < 1 ? 1 : (kValues / regs) > kBlocks ? kBlocks : (kValues / regs);
     const int c_l = mfma_out_col(g, lane);
@@ -736,6 +737,38 @@ __global__ void __launch_bounds__(256) sgemm_scale_tiles_kernel(KernelArgs p) {
   }
 }
 
+// The configuration whose geometry the K loop runs with: the tuple itself,
+// or for a k-sliced tuple the same tile at half the threads (one wave group).
+template <class Cfg, bool KS = (Cfg::OPT & kOptKSlice) != 0>
+struct LoopCfg {
+  using type = Cfg;
+};
+template <class Cfg>
+struct LoopCfg<Cfg, true> {
+  using type = TileCfg<Cfg::BM, Cfg::BN, Cfg::BK, Cfg::WM, Cfg::WN, Cfg::WNITER, Cfg::TM, Cfg::TN,
+                       Cfg::NT / 2, Cfg::PATH, Cfg::tile.swz, Cfg::OPT & ~kOptKSlice>;
+};
+
+// Accumulator e of a lane (the order epilogue_atomic and owner() use).
+template <class Cfg>
+__device__ __forceinline__ float acc_get(const Acc<Cfg>& acc, int e) {
+  if constexpr (Cfg::PATH == kPathValu) {
+    return acc.v[e];
+  } else {
+    constexpr int regs = Cfg::PATH == kPathMfma32 ? 16 : 4;
+    return acc.v[(e / regs) / Cfg::WNITER][(e / regs) % Cfg::WNITER][e % regs];
+  }
+}
+template <class Cfg>
+__device__ __forceinline__ void acc_add(Acc<Cfg>& acc, int e, float x) {
+  if constexpr (Cfg::PATH == kPathValu) {
+    acc.v[e] += x;
+  } else {
+    constexpr int regs = Cfg::PATH == kPathMfma32 ? 16 : 4;
+    acc.v[(e / regs) / Cfg::WNITER][(e / regs) % Cfg::WNITER][e % regs] += x;
+  }
+}
+
 // The body of the tile kernel (one workgroup, one output tile or K segment).
 template <class Cfg, bool VEC>
 __device__ __forceinline__ void tile_body(const KernelArgs& p) {
@@ -743,11 +776,28 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
   static_assert(tile_legal(Cfg::tile), "illegal tile tuple instantiated");
   constexpr bool kDirect = (Cfg::OPT & kOptDirectLds) != 0;
   constexpr int kStages = kDirect ? stages_of(Cfg::tile) : 2;
-  __shared__ __attribute__((aligned(16))) float lds[kStages * g.STAGE];
+  // K-sliced tuples: two wave groups, each with its own LDS ring, run the K
+  // loop over the two halves of the slice range with the geometry of half
+  // the workgroup (L), and their partial sums are added in LDS afterwards.
+  // Every other tuple runs the loop with its own geometry (L = Cfg).
+  constexpr bool kKSlice = (Cfg::OPT & kOptKSlice) != 0;
+  using L = typename LoopCfg<Cfg>::type;
+  constexpr Geom lg = make_geom(L::tile);
+  __shared__ __attribute__((aligned(16))) float lds[(kKSlice ? 2 : 1) * kStages * g.STAGE];
 
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  // A k-sliced tuple's waves form two groups of kGroupWaves: `half` is the
+  // group, `wave` the index within it, and `ro` the offset (floats) of the
+  // group's LDS stages.  (All constants of the tuple otherwise; kept as
+  // const values selected at compile time, because mutable copies of the
+  // wave index or of the LDS pointer change the code the compiler generates
+  // for every tuple.)
+  constexpr int kGroupWaves = Cfg::NT / (kKSlice ? 128 : 64);
+  const int raw_wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int half = kKSlice ? (raw_wave >= kGroupWaves ? 1 : 0) : 0;
+  const int wave = kKSlice ? raw_wave - half * kGroupWaves : raw_wave;
+  const int ro = kKSlice ? half * kStages * g.STAGE : 0;
   constexpr bool kXcd = (Cfg::OPT & kOptXcdRemap) != 0;
   // Whole tiles first (one workgroup each), then the K segments of the split
   // tiles.
@@ -770,9 +820,17 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
   const TileRC tc = tile_at(pos, p.tiles_m, p.tiles_n, p.group_m, kXcd);
   const int row0 = tc.r * g.BM;
   const int col0 = tc.c * g.BN;
+  // The two groups of a k-sliced tuple run the same number of slices (the
+  // second one's last slice lies past K when the count is odd, and loads
+  // zeros), so their barriers pair up.
+  if constexpr (kKSlice) {
+    const int n0 = (kt1 - kt0 + 1) / 2;
+    kt0 += half * n0;
+    kt1 = kt0 + n0;
+  }
   const int wr0 = wave_row0(g, wave), wc0 = wave_col0(g, wave);
 
-  Acc<Cfg> acc;
+  Acc<L> acc;
   acc_zero(acc);
 
   if constexpr (kDirect) {
@@ -785,20 +843,20 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
     // past K load nothing (zeros); past a segment's end they load the next
     // segment's slices, which no one reads.
     constexpr int S = kStages;
-    constexpr int kInFlight = (S - 2) * dma_ops_per_slice(Cfg::tile, VEC ? 4 : 1);
-    const int r = tail_width(p, g.BK);
-    DmaLanes<Cfg, VEC> d;
-    dma_setup<Cfg, VEC>(p, col0, wave, lane, d);
+    constexpr int kInFlight = (S - 2) * dma_ops_per_slice(L::tile, VEC ? 4 : 1);
+    const int r = tail_width(p, lg.BK);
+    DmaLanes<L, VEC> d;
+    dma_setup<L, VEC>(p, col0, wave, lane, d);
 #pragma unroll
     for (int i = 0; i < S - 1; ++i) {
       if (i == 0 && kt0 == 0)
-        dma_first_slice<Cfg, VEC>(p, lds, row0, col0, r, wave, lane);
+        dma_first_slice<L, VEC>(p, lds + ro, row0, col0, r, wave, lane);
       else
-        dma_slice<Cfg, VEC>(p, d, lds + i * g.STAGE, row0, col0, slice_k0(kt0 + i, r, g.BK), wave);
+        dma_slice<L, VEC>(p, d, lds + ro + i * lg.STAGE, row0, col0, slice_k0(kt0 + i, r, lg.BK), wave);
     }
     ring_barrier<kInFlight>();
     int cur = 0, nxt = S - 1;
-    if constexpr ((Cfg::OPT & kOptPipelined) != 0) {
+    if constexpr ((L::OPT & kOptPipelined) != 0) {
       // Fragments one k-group ahead; the slice's last group is multiplied
       // after the barrier, behind the reads of the next slice's first group
       // (those registers were read before the barrier, so the stage they
@@ -811,14 +869,14 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
       // past K) or, on the 32x32 path's 256x256 tiles in the float4 variant,
       // bands of the wave's C tile that the epilogue reads first
       // (dma_c_band).
-      constexpr int KG = g.BK / dma_kgroup(g);
+      constexpr int KG = lg.BK / dma_kgroup(lg);
       // The C prefetch of the last slices pays on the 256x256 tiles of the
       // 32x32 path (one long K loop per tile, C read after it); on smaller
       // tiles the one-at-a-time tail it needs costs more than it saves.
-      constexpr bool kCPrefetch = VEC && S == 2 && Cfg::PATH == kPathMfma32 && g.BM * g.BN >= 256 * 256;
-      DmaFrag<Cfg> f[2];
-      dma_frag_load<Cfg>(lds, 0, wr0, wc0, lane, f[0]);
-      dma_slice<Cfg, VEC>(p, d, lds + (S - 1) * g.STAGE, row0, col0, slice_k0(kt0 + S - 1, r, g.BK), wave);
+      constexpr bool kCPrefetch = VEC && S == 2 && L::PATH == kPathMfma32 && lg.BM * lg.BN >= 256 * 256;
+      DmaFrag<L> f[2];
+      dma_frag_load<L>(lds + ro, 0, wr0, wc0, lane, f[0]);
+      dma_slice<L, VEC>(p, d, lds + ro + (S - 1) * lg.STAGE, row0, col0, slice_k0(kt0 + S - 1, r, lg.BK), wave);
       // One slice with stage cs being multiplied.  With two stages the K
       // loop runs two slices per iteration, so each one's stages are
       // constants and its fragment reads take fixed addresses with immediate
@@ -826,28 +884,28 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
       // variant, whose four times as many load offsets leave no registers
       // for the second copy.
       auto slice = [&](int kt, int cs, bool c_band = false) __attribute__((always_inline)) {
-        const float* st = lds + cs * g.STAGE;
+        const float* st = lds + ro + cs * lg.STAGE;
         // The scheduling barriers keep each group's reads ahead of the
         // previous group's MFMAs (left alone, the compiler sinks every read
         // to just before its first use and waits for it there).
 #pragma unroll
         for (int kg = 0; kg + 1 < KG; ++kg) {
-          dma_frag_load<Cfg>(st, kg + 1, wr0, wc0, lane, f[(kg + 1) & 1]);
+          dma_frag_load<L>(st, kg + 1, wr0, wc0, lane, f[(kg + 1) & 1]);
           __builtin_amdgcn_sched_barrier(0);
-          dma_frag_mfma<Cfg>(f[kg & 1], acc);
+          dma_frag_mfma<L>(f[kg & 1], acc);
         }
         ring_barrier<kInFlight>();
-        dma_frag_load<Cfg>(lds + (cs + 1 == S ? 0 : cs + 1) * g.STAGE, 0, wr0, wc0, lane, f[KG & 1]);
+        dma_frag_load<L>(lds + ro + (cs + 1 == S ? 0 : cs + 1) * lg.STAGE, 0, wr0, wc0, lane, f[KG & 1]);
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (kCPrefetch) {
           if (c_band)
-            dma_c_band<Cfg>(p, lds + cs * g.STAGE, row0 + wr0, col0 + wc0, kt + S - kt1, wave, lane);
+            dma_c_band<L>(p, lds + ro + cs * lg.STAGE, row0 + wr0, col0 + wc0, kt + S - kt1, wave, lane);
           else
-            dma_slice<Cfg, VEC>(p, d, lds + cs * g.STAGE, row0, col0, slice_k0(kt + S, r, g.BK), wave);
+            dma_slice<L, VEC>(p, d, lds + ro + cs * lg.STAGE, row0, col0, slice_k0(kt + S, r, lg.BK), wave);
         } else {
-          dma_slice<Cfg, VEC>(p, d, lds + cs * g.STAGE, row0, col0, slice_k0(kt + S, r, g.BK), wave);
+          dma_slice<L, VEC>(p, d, lds + ro + cs * lg.STAGE, row0, col0, slice_k0(kt + S, r, lg.BK), wave);
         }
-        dma_frag_mfma<Cfg>(f[(KG - 1) & 1], acc);
+        dma_frag_mfma<L>(f[(KG - 1) & 1], acc);
         if constexpr ((KG & 1) != 0) f[0] = f[1];
       };
       if constexpr (S == 2 && VEC && kCPrefetch) {
@@ -875,9 +933,9 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
       }
     } else {
       auto slice = [&](int kt, int cs, int ns) __attribute__((always_inline)) {
-        dma_slice<Cfg, VEC>(p, d, lds + ns * g.STAGE, row0, col0, slice_k0(kt + S - 1, r, g.BK), wave);
-        if constexpr (!(Cfg::OPT & kOptFloatLoads)) __builtin_amdgcn_sched_barrier(0);
-        inner_product_dma<Cfg>(lds + cs * g.STAGE, wr0, wc0, lane, acc);
+        dma_slice<L, VEC>(p, d, lds + ro + ns * lg.STAGE, row0, col0, slice_k0(kt + S - 1, r, lg.BK), wave);
+        if constexpr (!(L::OPT & kOptFloatLoads)) __builtin_amdgcn_sched_barrier(0);
+        inner_product_dma<L>(lds + ro + cs * lg.STAGE, wr0, wc0, lane, acc);
         ring_barrier<kInFlight>();
       };
       if constexpr (S == 2 && VEC) {
@@ -896,7 +954,24 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
       }
     }
     // Nothing may still be writing this workgroup's LDS when its waves end.
-    if constexpr (kInFlight > 0 || (Cfg::OPT & kOptPipelined) != 0) wait_vmem<0>();
+    if constexpr (kInFlight > 0 || (L::OPT & kOptPipelined) != 0) wait_vmem<0>();
+    if constexpr (kKSlice) {
+      // The second group's partial sums reach the first through LDS (the
+      // rings are free once every wave has passed the barrier): stored
+      // lane-contiguous per accumulator, then added in a fixed order, so the
+      // result does not depend on timing.
+      wait_vmem<0>();
+      __syncthreads();
+      float* part = lds + wave * (lg.ACC * 64) + lane;
+      if (half == 1) {
+#pragma unroll
+        for (int e = 0; e < lg.ACC; ++e) part[e * 64] = acc_get(acc, e);
+      }
+      __syncthreads();
+      if (half == 1) return;
+#pragma unroll
+      for (int e = 0; e < lg.ACC; ++e) acc_add(acc, e, part[e * 64]);
+    }
   } else if constexpr ((Cfg::OPT & kOptPipelined) != 0) {
     k_loop_pipelined<Cfg, VEC>(p, lds, row0, col0, t, wr0, wc0, lane, kt0, kt1, acc);
   } else {
@@ -925,11 +1000,11 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
   float* cw = p.C + static_cast<long long>(row0 + wr0) * p.ldc + (col0 + wc0);
   if constexpr ((Cfg::OPT & kOptSplitK) != 0) {
     if (split) {
-      epilogue_atomic<Cfg>(cw, static_cast<int>(p.ldc), rlim, clim, lane, p.alpha, acc);
+      epilogue_atomic<L>(cw, static_cast<int>(p.ldc), rlim, clim, lane, p.alpha, acc);
       return;
     }
   }
-  epilogue<Cfg, VEC>(cw, static_cast<int>(p.ldc), rlim, clim, lane, p.alpha, p.beta, acc);
+  epilogue<L, VEC, Cfg>(cw, static_cast<int>(p.ldc), rlim, clim, lane, p.alpha, p.beta, acc);
 }
 
 template <class Cfg, bool VEC>

@@ -81,10 +81,25 @@ enum Opt : int {
   // pages give the second launch-bounds argument.
   kOptOccShift = 7,
   kOptOccMask = 3 << kOptOccShift,
-  kOptAll = 511,
+  // K-sliced workgroup (direct-LDS MFMA tuples): NT threads form two groups
+  // of NT/2 that each cover the whole block tile with their own LDS ring,
+  // over the two halves of the K slices; at the end the second group's
+  // accumulators are added to the first's through LDS (a fixed order, no
+  // atomics).  It doubles the waves per SIMD of a tile without a second
+  // output tile, for shapes with about one tile per compute unit.
+  kOptKSlice = 512,
+  kOptAll = 1023,
 };
 
 constexpr int stages_of(const Tile& t) { return 2 + ((t.opt & kOptStagesMask) >> kOptStagesShift); }
+
+// Wave groups a k-sliced tuple splits its K loop over (1 otherwise), and the
+// tuple one group runs: the same tile at NT / 2 threads without the option.
+constexpr int kslices_of(const Tile& t) { return (t.opt & kOptKSlice) ? 2 : 1; }
+constexpr Tile half_tile(const Tile& t) {
+  return Tile{t.BM, t.BN, t.BK, t.WM, t.WN, t.WNITER, t.TM, t.TN, t.NT / 2, t.path, t.swz,
+              t.opt & ~kOptKSlice};
+}
 
 // Workgroups per CU the tuple asks for (0 = no request), and the waves per
 // SIMD that implies (1 = the compiler's default).
@@ -162,7 +177,8 @@ enum Reason : int {
                             // BK in {8, 16, 32, 64} (16 up for 16x16x4), or a stage ring
                             // without direct-LDS staging,
                             // of 5 stages, or with more loads in flight than vmcnt counts, or a
-                            // residency request beyond 8 waves per SIMD or the CU's LDS
+                            // residency request beyond 8 waves per SIMD or the CU's LDS, or a
+                            // k-sliced tuple off the direct-LDS MFMA path or with split-K
   kNumReasons = 20,
 };
 
@@ -187,7 +203,7 @@ constexpr int lds_floats_per_stage(const Tile& t) {
 constexpr int lds_bytes(const Tile& t, const Target& m) {
   const int buffers = (t.opt & kOptDirectLds) && stages_of(t) > m.lds_buffers ? stages_of(t)
                                                                                : m.lds_buffers;
-  return buffers * lds_floats_per_stage(t) * 4;
+  return kslices_of(t) * buffers * lds_floats_per_stage(t) * 4;
 }
 
 // Registers that hold one staged tile between its global load and its LDS
@@ -213,7 +229,43 @@ constexpr int vgpr_estimate(const Tile& t, int wave) {
   return 2 * ksteps * (wmiter + t.WNITER) + prefetch_regs(t) + fixed;
 }
 
+// One workgroup puts ceil(NT / 256) waves on each of a CU's 4 SIMDs, which
+// share the SIMD's 512 registers per lane.
+constexpr int check_registers(const Tile& t, const Target& m) {
+  const int est = vgpr_estimate(t, m.wave);
+  const int per_simd = (t.NT / m.wave + 3) / 4;
+  const int budget = m.max_vgpr / per_simd;
+  if (t.path == kPathValu) {
+    if (est > m.max_arch_vgpr || est > budget) return kRegisterEstimate;
+  } else {
+    const int total = est + acc_per_lane(t, m.wave);
+    if (est > m.max_arch_vgpr || total > m.max_vgpr || total > budget) return kRegisterEstimate;
+  }
+  return kLegal;
+}
+
+constexpr int check_tile(const Tile& t, const Target& m);
+
+// A k-sliced tuple is legal when one wave group's tuple is, the option sits
+// on a direct-LDS MFMA tuple without the split-K tail (whose segments would
+// cross the groups' K ranges), both rings fit the LDS, the second group's
+// partial sums (BM x BN floats) fit inside them, and the registers fit with
+// both groups' waves on the SIMDs.
+constexpr int check_kslice(const Tile& t, const Target& m) {
+  if (t.NT <= 0 || t.NT > 1024) return kBadRange;
+  if (t.NT % (2 * m.wave) != 0) return kThreadsNotWaves;
+  if (t.path == kPathValu || !(t.opt & kOptDirectLds) || (t.opt & kOptSplitK)) return kBadOptions;
+  const int h = check_tile(half_tile(t), m);
+  if (h != kLegal) return h;
+  if (lds_bytes(t, m) > m.lds_bytes || t.BM * t.BN * 4 > lds_bytes(t, m)) return kLdsOverflow;
+  if (min_blocks_of(t) > 0 &&
+      (waves_per_eu_of(t) > 8 || min_blocks_of(t) * lds_bytes(t, m) > m.lds_bytes))
+    return kBadOptions;
+  return m.gfx950_rules ? check_registers(t, m) : kLegal;
+}
+
 constexpr int check_tile(const Tile& t, const Target& m) {
+  if (t.opt & kOptKSlice) return check_kslice(t, m);
   if (t.BM <= 0 || t.BN <= 0 || t.BK <= 0 || t.WM <= 0 || t.WN <= 0 || t.WNITER <= 0 ||
       t.TM <= 0 || t.TN <= 0 || t.NT <= 0 || t.NT > 1024 || t.BM > kMaxTileRows ||
       t.BK > kMaxTileRows)
@@ -307,19 +359,7 @@ constexpr int check_tile(const Tile& t, const Target& m) {
   const int acc_limit = (t.path == kPathValu) ? (m.max_acc < 128 ? m.max_acc : 128) : m.max_acc;
   if (acc_per_lane(t, m.wave) > acc_limit) return kAccOverflow;
 
-  if (m.gfx950_rules) {
-    // One workgroup puts ceil(NT / 256) waves on each of a CU's 4 SIMDs, which
-    // share the SIMD's 512 registers per lane.
-    const int est = vgpr_estimate(t, m.wave);
-    const int per_simd = (t.NT / m.wave + 3) / 4;
-    const int budget = m.max_vgpr / per_simd;
-    if (t.path == kPathValu) {
-      if (est > m.max_arch_vgpr || est > budget) return kRegisterEstimate;
-    } else {
-      const int total = est + acc_per_lane(t, m.wave);
-      if (est > m.max_arch_vgpr || total > m.max_vgpr || total > budget) return kRegisterEstimate;
-    }
-  }
+  if (m.gfx950_rules) return check_registers(t, m);
   return kLegal;
 }
 

@@ -119,7 +119,9 @@ typedef struct sgemm_config_t {
                   reproducible), bit 4 direct global-to-LDS loads (both MFMA paths;
                   16-byte loads in the float4 variant, 4-byte loads in the scalar one),
                   bits 5-6 with bit 4: LDS stages - 2, bits 7-8: workgroups per CU
-                  requested - 1 (0 = none) */
+                  requested - 1 (0 = none), bit 9 k-sliced workgroup (with bit 4:
+                  two wave groups of NT/2 threads split the K slices and add their
+                  partial sums in LDS, in a fixed order) */
   int32_t WMITER, WSUBM, WSUBN;
   int32_t acc_per_lane;
   int32_t lds_bytes;     /* all LDS stages */

@@ -82,6 +82,29 @@ def test_each_guard_trips(reason, tup):
     assert fg.check_tuple(tup, "gfx950") == reason
 
 
+def test_kslice_rules():
+    # K-sliced workgroups: legal exactly when one wave group's tuple is, on
+    # the direct-LDS MFMA path without split-K, with both groups' LDS rings
+    # (and the partial-sum buffer) inside the CU's LDS.
+    ks = 512
+    base = (64, 64, 64, 32, 32, 1, 16, 1, 512, MFMA32, 32)
+    assert fg.check_tuple(base + (16 | ks,), "gfx950") == 0
+    assert fg.check_tuple(base[:8] + (256,) + base[9:] + (16,), "gfx950") == 0  # one group's tuple
+    assert fg.check_tuple(base + (ks,), "gfx950") == 19            # not direct-LDS
+    assert fg.check_tuple(base + (16 | 8 | ks,), "gfx950") == 19   # with split-K
+    assert fg.check_tuple((128, 64, 16, 64, 64, 2, 4, 4, 256, VALU, 32, ks), "gfx950") == 19
+    assert fg.check_tuple(base[:8] + (384,) + base[9:] + (16 | ks,), "gfx950") == 4  # 3 waves per group
+    # 128 x 128 x 64: two rings of two 64 KiB stages exceed 160 KiB.
+    assert fg.check_tuple((128, 128, 64, 64, 64, 2, 16, 1, 512, MFMA32, 32, 16 | ks), "gfx950") == 13
+    # 256 x 256 x 8: the rings fit, the 256 KiB partial-sum buffer does not.
+    assert fg.check_tuple((256, 256, 8, 128, 128, 4, 16, 1, 512, MFMA32, 32, 16 | ks), "gfx950") == 13
+    for c in fg.configs():
+        if c["opt"] & ks:
+            half = c["tuple"][:8] + (c["NT"] // 2,) + c["tuple"][9:11] + (c["opt"] & ~ks,)
+            assert fg.check_tuple(half, "gfx950") == 0, c["tuple"]
+            assert c["lds_bytes"] >= c["BM"] * c["BN"] * 4
+
+
 def test_tile_height_limit():
     # In-tile offsets are 32-bit: a block tile taller than 256 rows at the
     # largest leading dimension (2^21 - 1) would leave a buffer resource's
