@@ -43,6 +43,9 @@ def parse():
                     help="only time the CPU oracle on every workload (one JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--ramp", action="store_true",
+                    help="only time, after an idle gap, 30 back-to-back launches of this library "
+                         "and of the vendor library one by one (clock ramp; one JSON line)")
     return ap.parse_args()
 
 
@@ -176,6 +179,38 @@ def kernel_resources(fg, info, plan, dev):
             "compute_units": cus, "threads_per_workgroup": info["NT"]}
 
 
+def ramp(fg, inputs, w, dev, launches=30, idle_s=3.0, rounds=2):
+    """Per-launch times of back-to-back launches after an idle gap, for this
+    library and for the vendor library in turn: how long the clock takes to
+    settle, and whether it settles the same way for both."""
+    import numpy as np
+    import torch
+    A, B, C = inputs.make(w)
+    Ad, Bd, C0 = (torch.from_numpy(x).to(dev) for x in (A, B, C))
+    Cs = [C0.clone() for _ in range(launches)]
+    stream = torch.cuda.current_stream(dev)
+    fg.sgemm_ex(Ad, Bd, Cs[0], w.alpha, w.beta, stream=stream)   # first-use set-up, untimed
+    torch.mm(Ad, Bd, out=Cs[0])
+    out = {"workload": w.name, "launches": launches, "idle_s": idle_s, "series": []}
+    for r in range(rounds):
+        for name, f in (("vendor torch.mm", lambda Cx: torch.mm(Ad, Bd, out=Cx)),
+                        ("this library", lambda Cx: fg.sgemm_ex(Ad, Bd, Cx, w.alpha, w.beta,
+                                                               stream=stream))):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(launches + 1)]
+            torch.cuda.synchronize()
+            time.sleep(idle_s)
+            ev[0].record(stream)
+            for i in range(launches):
+                f(Cs[i])
+                ev[i + 1].record(stream)
+            torch.cuda.synchronize()
+            ms = [round(ev[i].elapsed_time(ev[i + 1]), 4) for i in range(launches)]
+            out["series"].append({"round": r, "kernel": name, "ms": ms,
+                                  "first5_median": float(np.median(ms[:5])),
+                                  "last5_median": float(np.median(ms[-5:]))})
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -212,6 +247,9 @@ def main():
     w = inputs.WORKLOADS[args.workload]
     if args.ladder:
         ladder(fg, inputs, model, w, dev, args)
+        return
+    if args.ramp:
+        ramp(fg, inputs, w, dev)
         return
     A, B, C = inputs.make(w)
     Ad = torch.from_numpy(A).to(dev)
