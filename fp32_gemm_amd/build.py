@@ -261,6 +261,13 @@ def _all_candidates():
             out.append(base + (swz, 0))
             if base[9] != VALU:
                 out.append(base + (swz, 3))
+    # One wave per SIMD with the whole 128 x 128 wave tile in accumulator
+    # registers, k-group pipelined.
+    for base in [(256, 256, 32, 128, 128, 4, 16, 1, 256, MFMA32, 32),
+                 (256, 256, 16, 128, 128, 4, 16, 1, 256, MFMA32, 32),
+                 (256, 256, 32, 128, 128, 8, 4, 1, 256, MFMA16, 32),
+                 (256, 256, 32, 128, 128, 8, 4, 1, 256, MFMA16, 64)]:
+        out += [base + (opt,) for opt in (17, 19, 25, 27)]
     # K-sliced workgroups (opt bit 9): two wave groups split the K slices of
     # one tile, for shapes with about one tile per compute unit.
     KS = 512
