@@ -268,6 +268,20 @@ def _all_candidates():
                  (256, 256, 32, 128, 128, 8, 4, 1, 256, MFMA16, 32),
                  (256, 256, 32, 128, 128, 8, 4, 1, 256, MFMA16, 64)]:
         out += [base + (opt,) for opt in (17, 19, 25, 27)]
+    # Direct-LDS staging on the VALU path (A transposed by 4-byte loads), on
+    # the register-staged sweep's best VALU tiles: 2 and 3 LDS stages, plain
+    # and XCD-aware order.
+    for base in [(256, 256, 16, 128, 64, 2, 4, 4, 512, VALU, 32),
+                 (256, 256, 8, 32, 256, 1, 8, 4, 512, VALU, 32),
+                 (256, 128, 16, 128, 64, 1, 4, 8, 256, VALU, 32),
+                 (128, 128, 16, 128, 64, 1, 4, 8, 128, VALU, 32),
+                 (128, 256, 16, 128, 64, 2, 4, 4, 256, VALU, 32),
+                 (128, 256, 16, 32, 128, 2, 4, 4, 512, VALU, 32),
+                 (128, 256, 32, 64, 64, 2, 8, 4, 512, VALU, 32),
+                 (256, 256, 16, 128, 64, 1, 4, 8, 512, VALU, 32),
+                 (128, 128, 16, 64, 64, 1, 8, 8, 256, VALU, 32),
+                 (128, 128, 32, 64, 32, 1, 8, 4, 512, VALU, 32)]:
+        out += [base + (opt,) for opt in (16, 18, 48, 50)]
     # K-sliced workgroups (opt bit 9): two wave groups split the K slices of
     # one tile, for shapes with about one tile per compute unit.
     KS = 512

@@ -183,7 +183,9 @@ template <class Cfg, bool VEC>
 struct DmaLanes {
   static constexpr Geom g = make_geom(Cfg::tile);
   static constexpr int FPL = VEC ? 4 : 1;
-  int a_off[dma_ops_a(g, FPL)];
+  // The VALU path loads its transposed A 4 bytes per lane in both variants.
+  static constexpr int FPL_A = Cfg::PATH == kPathValu ? 1 : FPL;
+  int a_off[dma_ops_a(g, FPL_A)];
   int b_off[dma_ops_b(g, FPL)];
 };
 
@@ -191,12 +193,13 @@ template <class Cfg, bool VEC>
 __device__ __forceinline__ void dma_setup(const KernelArgs& p, int col0, int wave, int lane,
                                           DmaLanes<Cfg, VEC>& d) {
   constexpr Geom g = make_geom(Cfg::tile);
-  constexpr int FPL = DmaLanes<Cfg, VEC>::FPL;
+  constexpr int FPL = DmaLanes<Cfg, VEC>::FPL, FPL_A = DmaLanes<Cfg, VEC>::FPL_A;
   const int lda = static_cast<int>(p.lda), ldb = static_cast<int>(p.ldb);
   const int cols = p.N - col0;
 #pragma unroll
-  for (int j = 0; j < dma_ops_a(g, FPL); ++j) {
-    const MK s = dma_a_src(g, dma_op(g, wave, j), lane, FPL);
+  for (int j = 0; j < dma_ops_a(g, FPL_A); ++j) {
+    const MK s = Cfg::PATH == kPathValu ? dma_at_src(g, dma_op(g, wave, j), lane)
+                                        : dma_a_src(g, dma_op(g, wave, j), lane, FPL);
     d.a_off[j] = (s.m * lda + s.k) * 4;
   }
 #pragma unroll
@@ -224,8 +227,8 @@ template <class Cfg, bool VEC, int PART = 0, int PARTS = 1>
 __device__ __forceinline__ void dma_slice(const KernelArgs& p, const DmaLanes<Cfg, VEC>& d,
                                           float* stage, int row0, int col0, int k0, int wave) {
   constexpr Geom g = make_geom(Cfg::tile);
-  constexpr int FPL = DmaLanes<Cfg, VEC>::FPL;
-  constexpr int NA = dma_ops_a(g, FPL), NB = dma_ops_b(g, FPL);
+  constexpr int FPL = DmaLanes<Cfg, VEC>::FPL, FPL_A = DmaLanes<Cfg, VEC>::FPL_A;
+  constexpr int NA = dma_ops_a(g, FPL_A), NB = dma_ops_b(g, FPL);
   constexpr int U0 = PART * (NA + NB) / PARTS, U1 = (PART + 1) * (NA + NB) / PARTS;
   const int kr = p.K - k0;
   // Sizes are multiplied by an opaque 0/1 rather than selected: the compiler
@@ -240,7 +243,7 @@ __device__ __forceinline__ void dma_slice(const KernelArgs& p, const DmaLanes<Cf
                               live * ((static_cast<long long>(rows - 1) * p.lda + kr) * 4));
 #pragma unroll
     for (int j = U0; j < (U1 < NA ? U1 : NA); ++j)
-      dma_load<VEC>(ra, stage + dma_op(g, wave, j) * 64 * FPL, d.a_off[j]);
+      dma_load<VEC && FPL_A == 4>(ra, stage + dma_op(g, wave, j) * 64 * FPL_A, d.a_off[j]);
   }
   if constexpr (U1 > NA) {
     const int krows = min(g.BK, kr);
@@ -289,15 +292,17 @@ __device__ __forceinline__ void dma_first_slice(const KernelArgs& p, float* stag
                                                 int col0, int r, int wave, int lane) {
   constexpr Geom g = make_geom(Cfg::tile);
   constexpr int FPL = VEC ? 4 : 1;
+  constexpr int FPL_A = Cfg::PATH == kPathValu ? 1 : FPL;
   const int lda = static_cast<int>(p.lda), ldb = static_cast<int>(p.ldb);
   const int rows = min(g.BM, p.M - row0);
   const auto ra = make_rsrc(p.A + static_cast<long long>(row0) * p.lda,
                             r > 0 ? (static_cast<long long>(rows - 1) * p.lda + r) * 4 : 0);
 #pragma unroll
-  for (int j = 0; j < dma_ops_a(g, FPL); ++j) {
-    const MK s = dma_a_src(g, dma_op(g, wave, j), lane, FPL);
-    dma_load<VEC>(ra, stage + dma_op(g, wave, j) * 64 * FPL,
-                  s.k < r ? (s.m * lda + s.k) * 4 : kMaskedOffset);
+  for (int j = 0; j < dma_ops_a(g, FPL_A); ++j) {
+    const MK s = Cfg::PATH == kPathValu ? dma_at_src(g, dma_op(g, wave, j), lane)
+                                        : dma_a_src(g, dma_op(g, wave, j), lane, FPL);
+    dma_load<VEC && FPL_A == 4>(ra, stage + dma_op(g, wave, j) * 64 * FPL_A,
+                                s.k < r ? (s.m * lda + s.k) * 4 : kMaskedOffset);
   }
   const auto rb = make_rsrc(p.B + col0,
                             r > 0 ? (static_cast<long long>(r - 1) * p.ldb + (p.N - col0)) * 4 : 0);
@@ -935,7 +940,12 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
       auto slice = [&](int kt, int cs, int ns) __attribute__((always_inline)) {
         dma_slice<L, VEC>(p, d, lds + ro + ns * lg.STAGE, row0, col0, slice_k0(kt + S - 1, r, lg.BK), wave);
         if constexpr (!(L::OPT & kOptFloatLoads)) __builtin_amdgcn_sched_barrier(0);
-        inner_product_dma<L>(lds + ro + cs * lg.STAGE, wr0, wc0, lane, acc);
+        // The VALU path reads its transposed A and Bs as register staging
+        // lays them out; the MFMA paths read the [m][k] chunk layout.
+        if constexpr (L::PATH == kPathValu)
+          inner_product<L>(lds + ro + cs * lg.STAGE, wr0, wc0, lane, acc);
+        else
+          inner_product_dma<L>(lds + ro + cs * lg.STAGE, wr0, wc0, lane, acc);
         ring_barrier<kInFlight>();
       };
       if constexpr (S == 2 && VEC) {

@@ -62,11 +62,14 @@ enum Opt : int {
   // of C by beta.  Those tiles' sums are therefore not bitwise reproducible
   // from run to run (they stay within the parity bound).
   kOptSplitK = 8,
-  // MFMA paths: global -> LDS with buffer loads that write LDS directly (no
-  // register round-trip, no ds_write; 16-byte loads in the float4 variant,
-  // 4-byte loads in the scalar variant), into an As[m][k] layout whose
-  // 16-byte chunks are XOR-swizzled by row; the inner product reads four k of
-  // A per 128-bit LDS read.
+  // Global -> LDS with buffer loads that write LDS directly (no register
+  // round-trip, no ds_write).  MFMA paths: 16-byte loads in the float4
+  // variant, 4-byte loads in the scalar variant, into an As[m][k] layout
+  // whose 16-byte chunks are XOR-swizzled by row; the inner product reads
+  // four k of A per 128-bit LDS read.  VALU path: A keeps the transposed,
+  // swizzled As[k][m] layout of register staging, filled by 4-byte loads (each
+  // lane fetches one row's element at one k), and B is loaded as on the MFMA
+  // paths; the inner product is unchanged.
   kOptDirectLds = 16,
   // Direct-LDS option only: a two-bit field giving the LDS stages of the ring,
   // 2 + its value (2, 3 or 4).  With S stages the loads of slice kt+S-1 are
@@ -111,9 +114,11 @@ constexpr int waves_per_eu_of(const Tile& t) {
 }
 
 // Direct-LDS instructions per wave and slice (A plus B) for fpl floats per
-// lane (4: float4 variant, 1: scalar variant).
+// lane (4: float4 variant, 1: scalar variant).  The VALU path loads its
+// transposed A 4 bytes per lane in both variants.
 constexpr int dma_ops_per_slice(const Tile& t, int fpl) {
-  return (t.BM * t.BK + t.BK * t.BN) / (fpl * t.NT);
+  const int fpl_a = t.path == kPathValu ? 1 : fpl;
+  return t.BM * t.BK / (fpl_a * t.NT) + t.BK * t.BN / (fpl * t.NT);
 }
 
 // Addressing limits.  The kernels form 64-bit tile base addresses but
@@ -173,8 +178,8 @@ enum Reason : int {
                             // when one workgroup puts several waves on each SIMD)
   kNoMfmaOnTarget = 18,
   kBadOptions = 19,         // unknown option bits, register-staged pipelining without an even
-                            // k-step count, direct-LDS staging on the VALU path, or without
-                            // BK in {8, 16, 32, 64} (16 up for 16x16x4), or a stage ring
+                            // k-step count, direct-LDS staging without BK in {8, 16, 32, 64}
+                            // (16 up for 16x16x4; BM % 64 == 0 on VALU), or a stage ring
                             // without direct-LDS staging,
                             // of 5 stages, or with more loads in flight than vmcnt counts, or a
                             // residency request beyond 8 waves per SIMD or the CU's LDS, or a
@@ -217,7 +222,9 @@ constexpr int vgpr_estimate(const Tile& t, int wave) {
   const int fixed = 28;  // addresses, loop state, masks, alpha/beta
   if (t.path == kPathValu) {
     const int frags = 2 * (wmiter * t.TM + t.WNITER * t.TN);
-    return acc_per_lane(t, wave) + frags + prefetch_regs(t) + fixed;
+    // Direct-LDS staging holds per-lane load offsets instead of a staged tile.
+    const int staging = (t.opt & kOptDirectLds) ? dma_ops_per_slice(t, 4) : prefetch_regs(t);
+    return acc_per_lane(t, wave) + frags + staging + fixed;
   }
   // MFMA: fragments are one register per (sub-tile row or column, k-step);
   // accumulators live in AccVGPRs.  Direct-LDS staging holds no staged
@@ -323,14 +330,15 @@ constexpr int check_tile(const Tile& t, const Target& m) {
   } else if (t.opt & kOptPipelined) {
     return kBadOptions;
   }
-  // Direct-LDS staging: the MFMA paths, in their own loop (pipelined by
+  // Direct-LDS staging: on the MFMA paths in their own loop (pipelined by
   // k-group rather than by k-step), with whole k-groups per slice (8 k for
   // 32x32x2, 16 for 16x16x4) and a power-of-two number of 16-byte chunks per
-  // As row (the chunk swizzle is an XOR below that count).
+  // As row (the chunk swizzle is an XOR below that count).  On the VALU path
+  // A stays transposed and each 4-byte load instruction fills 64 floats of
+  // one As row, so BM is a multiple of 64.
   if ((t.opt & kOptDirectLds) &&
-      (t.path == kPathValu ||
-       (t.BK != 8 && t.BK != 16 && t.BK != 32 && t.BK != 64) ||
-       (t.path == kPathMfma16 && t.BK < 16)))
+      ((t.BK != 8 && t.BK != 16 && t.BK != 32 && t.BK != 64) ||
+       (t.path == kPathMfma16 && t.BK < 16) || (t.path == kPathValu && t.BM % 64 != 0)))
     return kBadOptions;
   // The stage ring belongs to the direct-LDS loop; at most 4 stages, and the
   // loads left in flight at each wait fit the 6-bit vmcnt counter.
@@ -341,11 +349,11 @@ constexpr int check_tile(const Tile& t, const Target& m) {
   if (m.gfx950_rules) {
     // The As/Bs XOR swizzle flips bits below swz, in steps of at least 4
     // words, so it needs swz-aligned rows and at most swz/4 groups of four
-    // k-rows per staged tile.  Direct-LDS tuples keep As as [m][k] with their
-    // own chunk swizzle; for them only the Bs part applies.
+    // k-rows per staged tile.  Direct-LDS MFMA tuples keep As as [m][k] with
+    // their own chunk swizzle; for them only the Bs part applies.
     if (t.swz != 0 && t.swz != 32 && t.swz != 64) return kSwizzleRange;
     if (t.swz != 0 && t.BN % t.swz != 0) return kSwizzleRange;
-    if (t.swz != 0 && !(t.opt & kOptDirectLds) &&
+    if (t.swz != 0 && (!(t.opt & kOptDirectLds) || t.path == kPathValu) &&
         (t.BM % t.swz != 0 || t.BK > t.swz || ((t.BK / 4) & (t.BK / 4 - 1)) != 0))
       return kSwizzleRange;
   }

@@ -155,6 +155,20 @@ FG_HD constexpr KN dma_b_src(const Geom& g, int i, int l, int fpl) {
   const int k = f / g.BN;
   return KN{k, (f % g.BN) ^ dma_swz_b(g, k)};
 }
+// Direct-LDS staging of A on the VALU path: the inner product reads A
+// transposed, As[k][m] (as_index), so these loads move 4 bytes per lane, in
+// both variants.  Lane l of A instruction i lands at float i*64 + l of the A
+// stage: k-row k = (i*64 + l) / SA at position j = (i*64 + l) % SA, which
+// as_index assigns to row m = j ^ swz_a(k).  The swizzle only flips bits
+// below 64 and BM is a multiple of 64, so an instruction's 64 floats stay in
+// one k-row and the lanes fetch a permutation of 64 consecutive rows at one
+// k.
+FG_HD constexpr MK dma_at_src(const Geom& g, int i, int l) {
+  const int w = i * 64 + l;
+  const int k = w / g.SA;
+  return MK{(w % g.SA) ^ swz_a(g, k), k};
+}
+
 // Fragments: an MFMA block of blk x blk outputs takes, per lane, one A and one
 // B value for each of its slots (2 for 32x32x2, 4 for 16x16x4; slot h =
 // lane / blk).  The slice's k run in groups of 4*slots; within group kg,

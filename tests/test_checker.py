@@ -196,18 +196,24 @@ def test_option_guard():
     # Pipelining is an MFMA-loop option and needs an even number of k-steps.
     assert fg.check_tuple((128, 64, 16, 64, 64, 2, 4, 4, 128, VALU, 32, 1)) == 19
     assert fg.check_tuple((128, 128, 4, 128, 64, 4, 4, 1, 128, MFMA16, 0, 1)) == 19
-    assert fg.check_tuple((128, 128, 16, 64, 64, 2, 16, 1, 256, MFMA32, 32, 512)) == 19  # unknown bit
+    assert fg.check_tuple((128, 128, 16, 64, 64, 2, 16, 1, 256, MFMA32, 32, 1024)) == 19  # unknown bit
     assert fg.check_tuple((128, 128, 16, 64, 64, 2, 16, 1, 256, MFMA32, 32, 3)) == 0
-    # Direct-LDS staging: the MFMA paths only, and BK a power of two from 8 to
-    # 64 (from 16 for 16x16x4, whose k-group is 16).  Its pipeline works per
-    # k-group, so an odd k-group count (one, here) is fine.
+    # Direct-LDS staging: BK a power of two from 8 to 64 (from 16 for
+    # 16x16x4, whose k-group is 16).  Its MFMA pipeline works per k-group, so
+    # an odd k-group count (one, here) is fine.  On the VALU path (A loaded
+    # transposed, 64 rows per load instruction) BM must be a multiple of 64,
+    # and the k-group pipeline does not apply.
     assert fg.check_tuple((128, 128, 16, 64, 64, 2, 16, 1, 256, MFMA32, 32, 16)) == 0
     assert fg.check_tuple((128, 128, 16, 64, 64, 2, 16, 1, 256, MFMA32, 32, 17)) == 0
     assert fg.check_tuple((128, 128, 8, 64, 64, 2, 16, 1, 256, MFMA32, 32, 17)) == 0
     assert fg.check_tuple((128, 128, 16, 64, 64, 4, 4, 1, 256, MFMA16, 32, 16)) == 0
     assert fg.check_tuple((128, 128, 16, 64, 64, 4, 4, 1, 256, MFMA16, 32, 17)) == 0
     assert fg.check_tuple((128, 128, 8, 64, 64, 4, 4, 1, 256, MFMA16, 32, 16)) == 19
-    assert fg.check_tuple((128, 64, 16, 64, 64, 2, 4, 4, 128, VALU, 32, 16)) == 19
+    assert fg.check_tuple((128, 64, 16, 64, 64, 2, 4, 4, 128, VALU, 32, 16)) == 0
+    assert fg.check_tuple((128, 64, 16, 64, 64, 2, 4, 4, 128, VALU, 32, 17)) == 19
+    assert fg.check_tuple((96, 64, 16, 96, 64, 2, 4, 4, 64, VALU, 32, 0)) == 0
+    assert fg.check_tuple((96, 64, 16, 96, 64, 2, 4, 4, 64, VALU, 32, 16)) == 19
+    assert fg.check_tuple((128, 64, 64, 64, 64, 2, 4, 4, 128, VALU, 32, 16)) == 16  # swizzle range
     assert fg.check_tuple((96, 64, 24, 32, 64, 2, 16, 1, 192, MFMA32, 0, 16)) == 19
     # Stage rings (opt field 32 = 3 stages, 64 = 4): direct-LDS only, at most 4
     # stages, and the LDS budget counts every stage.
