@@ -882,6 +882,11 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
       DmaFrag<L> f[2];
       dma_frag_load<L>(lds + ro, 0, wr0, wc0, lane, f[0]);
       dma_slice<L, VEC>(p, d, lds + ro + (S - 1) * lg.STAGE, row0, col0, slice_k0(kt0 + S - 1, r, lg.BK), wave);
+      // Drain the LDS queue once before the loop: entering it with other
+      // LDS work possibly pending makes the compiler wait for every LDS read
+      // (lgkmcnt(0)) at the head of each iteration instead of only for the
+      // fragments the first MFMAs use.
+      __builtin_amdgcn_s_waitcnt(0xc07f);
       // One slice with stage cs being multiplied.  With two stages the K
       // loop runs two slices per iteration, so each one's stages are
       // constants and its fragment reads take fixed addresses with immediate
