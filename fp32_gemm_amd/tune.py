@@ -81,7 +81,8 @@ def usable_configs(vector_variant=True):
 def tune_shape(w, dev, configs, log, finalists=6, progress=None):
     """Sweep one shape: exact check and short timing of every configuration,
     then the `finalists` fastest of each path re-timed interleaved with the
-    long protocol.  Returns (best overall, best per path, all records)."""
+    long protocol, path by path.  Returns (best overall, best per path, all
+    records)."""
     A, B, C = inputs.make(w)
     Ad, Bd = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
     Cd = torch.from_numpy(C).to(dev)
@@ -106,32 +107,36 @@ def tune_shape(w, dev, configs, log, finalists=6, progress=None):
     by_path = {}
     for r in sorted((r for r in results if r["exact"]), key=lambda r: r["ms"]):
         by_path.setdefault(r["path"], []).append(r)
-    ok = [r for rs in by_path.values() for r in rs[:finalists]]
-    # Finalists are timed interleaved (one batch of each in turn, repeated),
-    # so clock and temperature drift affect them alike.
+    # Each path's finalists are timed interleaved (one batch of each in turn,
+    # repeated), so clock and temperature drift affect them alike.  The
+    # paths are timed in separate groups: a VALU batch draws less power than
+    # an MFMA batch, and alternating the two shifts the clock between
+    # batches, which skewed the MFMA finalists' order by up to 2 %.
     warm, reps = LONG
     batch = 5
-    fns = [lambda r=r: fg.sgemm_ex(Ad, Bd, Cd, w.alpha, w.beta, stream=stream, cfg_id=r["cfg_id"])
-           for r in ok]
-    for f in fns:
-        for _ in range(warm):
-            f()
-    samples = [[] for _ in ok]
-    for _ in range(reps // batch):
-        for i, f in enumerate(fns):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(batch):
+    for group in by_path.values():
+        ok = group[:finalists]
+        fns = [lambda r=r: fg.sgemm_ex(Ad, Bd, Cd, w.alpha, w.beta, stream=stream,
+                                       cfg_id=r["cfg_id"]) for r in ok]
+        for f in fns:
+            for _ in range(warm):
                 f()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            samples[i].append(e0.elapsed_time(e1) / batch)
-    for r, smp in zip(ok, samples):
-        med = float(np.median(smp))
-        fin = dict(r, ms=med, ms_min=float(min(smp)), ms_max=float(max(smp)),
-                   tflops=flops / (med * 1e-3) / 1e12, protocol="long")
-        results.append(fin)
-        log(fin)
+        samples = [[] for _ in ok]
+        for _ in range(reps // batch):
+            for i, f in enumerate(fns):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(batch):
+                    f()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                samples[i].append(e0.elapsed_time(e1) / batch)
+        for r, smp in zip(ok, samples):
+            med = float(np.median(smp))
+            fin = dict(r, ms=med, ms_min=float(min(smp)), ms_max=float(max(smp)),
+                       tflops=flops / (med * 1e-3) / 1e12, protocol="long")
+            results.append(fin)
+            log(fin)
     longs = [r for r in results if r.get("protocol") == "long"]
     best_by_path = {}
     for r in longs:
@@ -150,8 +155,8 @@ def write_summary(best_by_shape_path, path, command, finalists=6):
              f"Command: `{command}`", "",
              "Every compiled, non-spilling configuration of each path was checked exactly on "
              "integer-valued inputs and timed with the short protocol (3 warm-up, 10 timed "
-             f"launches); the {finalists} fastest of each path were then re-timed interleaved (20 "
-             "warm-up, 12 batches of 5). Times are the long protocol's median.", "",
+             f"launches); the {finalists} fastest of each path were then re-timed interleaved, path "
+             "by path (20 warm-up, 12 batches of 5). Times are the long protocol's median.", "",
              "| shape | path | swept | best tuple (BM,BN,BK,WM,WN,WNITER,TM,TN,NT,path,swz,opt) "
              "| ms | TFLOP/s | % of 157.3 |",
              "|---|---|---|---|---|---|---|"]
