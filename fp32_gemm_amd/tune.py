@@ -168,6 +168,59 @@ def write_summary(best_by_shape_path, path, command, finalists=6):
         f.write("\n".join(lines) + "\n")
 
 
+def retime(names, shapes, dev, results_path, top, summary_path, command):
+    """Interleaved re-timing, per shape, of the tuned dispatch's choice and the
+    `top` fastest matrix-core tuples of a previous sweep (short protocol
+    records in `results_path`): 20 warm-up launches each, then rounds of one
+    5-launch batch of each in turn (30 rounds; 12 above 2 * 4096^3 FLOP)."""
+    recs = [json.loads(l) for l in open(results_path)]
+    ids = {c["tuple"]: c["id"] for c in fg.configs()}
+    stream = torch.cuda.current_stream(dev)
+    lines = ["# Tuned-table rules: interleaved re-timing against each shape's best sweep candidates", "",
+             f"Command: `{command}`", "",
+             f"Per shape: the tuned dispatch's choice (marked `*`) and the {top} fastest MFMA tuples of the "
+             "sweep in the results file, 20 warm-up launches each, then rounds of one 5-launch batch of "
+             "each in turn (30 rounds; 12 at 8192^3), on the workload's own inputs; medians in TFLOP/s.", "",
+             "| shape | tuple (BM,BN,BK,WM,WN,WNITER,TM,TN,NT,path,swz,opt) | TFLOP/s |", "|---|---|---|"]
+    for name in names:
+        w = shapes[name]
+        A, B, C = inputs.make(w)
+        Ad, Bd, Cd = (torch.from_numpy(x).to(dev) for x in (A, B, C))
+        chosen = fg.plan(w.M, w.N, w.K, Ad.data_ptr(), w.K, Bd.data_ptr(), w.N, Cd.data_ptr(),
+                         w.N)["cfg_id"]
+        chosen_t = fg.config_info(chosen)["tuple"]
+        short = sorted((r for r in recs if r["workload"] == name and r.get("protocol") == "short"
+                        and r["exact"] and r["path"] != "valu"), key=lambda r: r["ms"])
+        cands = list(dict.fromkeys([chosen_t] + [tuple(r["tuple"]) for r in short[:top]]))
+        cands = [t for t in cands if t in ids]
+        fns = [lambda i=ids[t]: fg.sgemm_ex(Ad, Bd, Cd, w.alpha, w.beta, stream=stream, cfg_id=i)
+               for t in cands]
+        for f in fns:
+            for _ in range(20):
+                f()
+        flops = model.flops(w.M, w.N, w.K)
+        rounds = 30 if flops <= 2 * 4096 ** 3 else 12
+        samples = [[] for _ in fns]
+        for _ in range(rounds):
+            for i, f in enumerate(fns):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(5):
+                    f()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                samples[i].append(e0.elapsed_time(e1) / 5)
+        rows = sorted(((flops / (float(np.median(v)) * 1e-3) / 1e12, t) for t, v in zip(cands, samples)),
+                      reverse=True)
+        for tf, t in rows:
+            mark = " *" if t == chosen_t else ""
+            lines.append(f"| {name} | {','.join(str(x) for x in t)}{mark} | {tf:.2f} |")
+            print(f"[retime] {name} {t}{mark} {tf:.2f} TFLOP/s", flush=True)
+    if summary_path:
+        with open(summary_path, "w") as f:
+            f.write("\n".join(lines) + "\n")
+
+
 def write_table(best_by_shape, path, defaults):
     lines = [
         "// tuned_table.inc -- dispatch table for the tuned choice of tile tuple.",
@@ -216,6 +269,9 @@ def main():
     ap.add_argument("--finalists", type=int, default=6,
                     help="tuples per path re-timed interleaved with the long protocol; the "
                          "sweep's short timings are noisier than the gaps between the best tuples")
+    ap.add_argument("--retime", default=None,
+                    help="re-time, per shape in --workloads, the tuned dispatch's choice against the "
+                         "--top fastest matrix-core tuples of this results file (no sweep)")
     ap.add_argument("--best", default=None,
                     help="print the best tuple recorded for this workload in --out and exit")
     args = ap.parse_args()
@@ -228,6 +284,11 @@ def main():
     torch.cuda.set_device(dev)
     if fg.device_check() != 0:
         raise SystemExit("tune: current device is not gfx950")
+    if args.retime:
+        shapes = {**inputs.WORKLOADS, **inputs.TUNING_EXTRA}
+        retime(args.workloads.split(","), shapes, dev, args.retime, args.top, args.summary_out,
+               "python -m fp32_gemm_amd.tune " + " ".join(sys.argv[1:]))
+        return 0
     paths = set(args.paths.split(","))
     configs = {v: [c for c in usable_configs(v) if c["path_name"] in paths] for v in (True, False)}
     if args.top_from:
