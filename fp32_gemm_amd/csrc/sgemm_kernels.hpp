@@ -314,6 +314,12 @@ __device__ __forceinline__ void dma_first_slice(const KernelArgs& p, float* stag
   }
 }
 
+// s_waitcnt immediate that waits for every LDS/scalar-memory operation of
+// the wave (lgkmcnt 0, bits 11:8) and leaves vector memory and exports
+// unconstrained (vmcnt 63 in bits 3:0 and 15:14, expcnt 7 in bits 6:4).  As a
+// builtin, unlike inline asm, the compiler's wait insertion accounts for it.
+constexpr int kWaitLgkm0 = 0xc07f;
+
 // Wait until at most N of this wave's vector memory operations are
 // outstanding (they complete in issue order).
 template <int N>
@@ -886,7 +892,7 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
       // LDS work possibly pending makes the compiler wait for every LDS read
       // (lgkmcnt(0)) at the head of each iteration instead of only for the
       // fragments the first MFMAs use.
-      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
       // One slice with stage cs being multiplied.  With two stages the K
       // loop runs two slices per iteration, so each one's stages are
       // constants and its fragment reads take fixed addresses with immediate
