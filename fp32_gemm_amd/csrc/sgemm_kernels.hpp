@@ -69,6 +69,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const float* base, l
                                            static_cast<int>(b), 0x00020000);
 }
 
+// A resource of `bytes` bytes (0 <= bytes <= kMaxRecords, which the caller
+// guarantees).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_exact(const float* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), static_cast<short>(0), bytes,
+                                           0x00020000);
+}
+
 __device__ __forceinline__ f32x4 buffer_load4(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
@@ -179,6 +186,15 @@ __device__ __forceinline__ int slice_k0(int kt, int r, int BK) {
 // resource (lda >= K), so they load as zero without being read.  Columns of B
 // past N would fall inside the resource (the next row's elements or ldb
 // padding), so their offsets are masked here, once.
+//
+// The tile's operand origins and resource extents are also fixed here, so a
+// slice's resources cost a few scalar additions: every slice after the first
+// is either whole (k0 + BK <= K) or lies past K, so the A resource of the
+// slice at k0 spans a_ext + (K - k0) * 4 bytes (the rows above the last one,
+// then the last row's elements from k0 to K) and the B resource b_ext bytes
+// (BK - 1 rows, then the in-range columns of the last one).  Both are below
+// kMaxBufferBytes (lda, ldb >= K, N and at most kMaxLeadingDim; BM, BK <=
+// kMaxTileRows), so they fit in 32 bits.
 template <class Cfg, bool VEC>
 struct DmaLanes {
   static constexpr Geom g = make_geom(Cfg::tile);
@@ -187,15 +203,24 @@ struct DmaLanes {
   static constexpr int FPL_A = Cfg::PATH == kPathValu ? 1 : FPL;
   int a_off[dma_ops_a(g, FPL_A)];
   int b_off[dma_ops_b(g, FPL)];
+  const float* a_row;  // &A[row0][0]
+  const float* b_col;  // &B[0][col0]
+  int a_ext, b_ext;
 };
 
 template <class Cfg, bool VEC>
-__device__ __forceinline__ void dma_setup(const KernelArgs& p, int col0, int wave, int lane,
-                                          DmaLanes<Cfg, VEC>& d) {
+__device__ __forceinline__ void dma_setup(const KernelArgs& p, int row0, int col0, int wave,
+                                          int lane, DmaLanes<Cfg, VEC>& d) {
   constexpr Geom g = make_geom(Cfg::tile);
   constexpr int FPL = DmaLanes<Cfg, VEC>::FPL, FPL_A = DmaLanes<Cfg, VEC>::FPL_A;
+  static_assert(g.BM <= kMaxTileRows && g.BK <= kMaxTileRows, "resource extents need 32 bits");
   const int lda = static_cast<int>(p.lda), ldb = static_cast<int>(p.ldb);
   const int cols = p.N - col0;
+  const int rows = min(g.BM, p.M - row0);
+  d.a_row = p.A + static_cast<long long>(row0) * p.lda;
+  d.b_col = p.B + col0;
+  d.a_ext = static_cast<int>(static_cast<long long>(rows - 1) * p.lda * 4);
+  d.b_ext = static_cast<int>((static_cast<long long>(g.BK - 1) * p.ldb + cols) * 4);
 #pragma unroll
   for (int j = 0; j < dma_ops_a(g, FPL_A); ++j) {
     const MK s = Cfg::PATH == kPathValu ? dma_at_src(g, dma_op(g, wave, j), lane)
@@ -225,30 +250,25 @@ __device__ __forceinline__ void dma_load(__amdgpu_buffer_rsrc_t r, float* dst, i
 // with vmcnt before the barrier that publishes the stage.
 template <class Cfg, bool VEC, int PART = 0, int PARTS = 1>
 __device__ __forceinline__ void dma_slice(const KernelArgs& p, const DmaLanes<Cfg, VEC>& d,
-                                          float* stage, int row0, int col0, int k0, int wave) {
+                                          float* stage, int k0, int wave) {
   constexpr Geom g = make_geom(Cfg::tile);
   constexpr int FPL = DmaLanes<Cfg, VEC>::FPL, FPL_A = DmaLanes<Cfg, VEC>::FPL_A;
   constexpr int NA = dma_ops_a(g, FPL_A), NB = dma_ops_b(g, FPL);
   constexpr int U0 = PART * (NA + NB) / PARTS, U1 = (PART + 1) * (NA + NB) / PARTS;
   const int kr = p.K - k0;
-  // Sizes are multiplied by an opaque 0/1 rather than selected: the compiler
-  // turns a select into a branch that duplicates the loads and cuts the loop
-  // body into separate scheduling regions.
-  int live1 = __builtin_amdgcn_readfirstlane(kr > 0 ? 1 : 0);
-  asm("" : "+s"(live1));
-  const long long live = live1;
+  // Sizes are masked with an opaque all-ones/zero word rather than selected:
+  // the compiler turns a select into a branch that duplicates the loads and
+  // cuts the loop body into separate scheduling regions.
+  int live = __builtin_amdgcn_readfirstlane(~((kr - 1) >> 31));  // -1 when kr > 0
+  asm("" : "+s"(live));
   if constexpr (U0 < NA) {
-    const int rows = min(g.BM, p.M - row0);
-    const auto ra = make_rsrc(p.A + static_cast<long long>(row0) * p.lda + k0,
-                              live * ((static_cast<long long>(rows - 1) * p.lda + kr) * 4));
+    const auto ra = make_rsrc_exact(d.a_row + k0, (d.a_ext + kr * 4) & live);
 #pragma unroll
     for (int j = U0; j < (U1 < NA ? U1 : NA); ++j)
       dma_load<VEC && FPL_A == 4>(ra, stage + dma_op(g, wave, j) * 64 * FPL_A, d.a_off[j]);
   }
   if constexpr (U1 > NA) {
-    const int krows = min(g.BK, kr);
-    const auto rb = make_rsrc(p.B + static_cast<long long>(k0) * p.ldb + col0,
-                              live * ((static_cast<long long>(krows - 1) * p.ldb + (p.N - col0)) * 4));
+    const auto rb = make_rsrc_exact(d.b_col + static_cast<long long>(k0) * p.ldb, d.b_ext & live);
 #pragma unroll
     for (int j = (U0 > NA ? U0 : NA) - NA; j < U1 - NA; ++j)
       dma_load<VEC>(rb, stage + g.BM * g.BK + dma_op(g, wave, j) * 64 * FPL, d.b_off[j]);
@@ -857,13 +877,13 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
     constexpr int kInFlight = (S - 2) * dma_ops_per_slice(L::tile, VEC ? 4 : 1);
     const int r = tail_width(p, lg.BK);
     DmaLanes<L, VEC> d;
-    dma_setup<L, VEC>(p, col0, wave, lane, d);
+    dma_setup<L, VEC>(p, row0, col0, wave, lane, d);
 #pragma unroll
     for (int i = 0; i < S - 1; ++i) {
       if (i == 0 && kt0 == 0)
         dma_first_slice<L, VEC>(p, lds + ro, row0, col0, r, wave, lane);
       else
-        dma_slice<L, VEC>(p, d, lds + ro + i * lg.STAGE, row0, col0, slice_k0(kt0 + i, r, lg.BK), wave);
+        dma_slice<L, VEC>(p, d, lds + ro + i * lg.STAGE, slice_k0(kt0 + i, r, lg.BK), wave);
     }
     ring_barrier<kInFlight>();
     int cur = 0, nxt = S - 1;
@@ -887,7 +907,7 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
       constexpr bool kCPrefetch = VEC && S == 2 && L::PATH == kPathMfma32 && lg.BM * lg.BN >= 256 * 256;
       DmaFrag<L> f[2];
       dma_frag_load<L>(lds + ro, 0, wr0, wc0, lane, f[0]);
-      dma_slice<L, VEC>(p, d, lds + ro + (S - 1) * lg.STAGE, row0, col0, slice_k0(kt0 + S - 1, r, lg.BK), wave);
+      dma_slice<L, VEC>(p, d, lds + ro + (S - 1) * lg.STAGE, slice_k0(kt0 + S - 1, r, lg.BK), wave);
       // Drain the LDS queue once before the loop: entering it with other
       // LDS work possibly pending makes the compiler wait for every LDS read
       // (lgkmcnt(0)) at the head of each iteration instead of only for the
@@ -917,9 +937,9 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
           if (c_band)
             dma_c_band<L>(p, lds + ro + cs * lg.STAGE, row0 + wr0, col0 + wc0, kt + S - kt1, wave, lane);
           else
-            dma_slice<L, VEC>(p, d, lds + ro + cs * lg.STAGE, row0, col0, slice_k0(kt + S, r, lg.BK), wave);
+            dma_slice<L, VEC>(p, d, lds + ro + cs * lg.STAGE, slice_k0(kt + S, r, lg.BK), wave);
         } else {
-          dma_slice<L, VEC>(p, d, lds + ro + cs * lg.STAGE, row0, col0, slice_k0(kt + S, r, lg.BK), wave);
+          dma_slice<L, VEC>(p, d, lds + ro + cs * lg.STAGE, slice_k0(kt + S, r, lg.BK), wave);
         }
         dma_frag_mfma<L>(f[(KG - 1) & 1], acc);
         if constexpr ((KG & 1) != 0) f[0] = f[1];
@@ -949,7 +969,7 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
       }
     } else {
       auto slice = [&](int kt, int cs, int ns) __attribute__((always_inline)) {
-        dma_slice<L, VEC>(p, d, lds + ro + ns * lg.STAGE, row0, col0, slice_k0(kt + S - 1, r, lg.BK), wave);
+        dma_slice<L, VEC>(p, d, lds + ro + ns * lg.STAGE, slice_k0(kt + S - 1, r, lg.BK), wave);
         if constexpr (!(L::OPT & kOptFloatLoads)) __builtin_amdgcn_sched_barrier(0);
         // The VALU path reads its transposed A and Bs as register staging
         // lays them out; the MFMA paths read the [m][k] chunk layout.
