@@ -345,6 +345,21 @@ constexpr int kWaitLgkm0 = 0xc07f;
 template <int N>
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
 
+// Orders the instructions of the scheduling region this call ends: its
+// vector memory reads (the slice's direct-to-LDS loads) spread evenly over
+// its MFMAs, one after every N_MFMA / N_VM of them.  Left to itself the
+// compiler issues the loads in runs of three or four between two MFMAs,
+// which stalls the wave's matrix work while they issue.
+template <int N_MFMA, int N_VM>
+__device__ __forceinline__ void spread_loads() {
+  constexpr int kStep = N_MFMA / N_VM;
+#pragma unroll
+  for (int i = 0; i < N_VM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, kStep, 0);  // kStep MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // one vector memory read
+  }
+}
+
 // Workgroup barrier of the direct-LDS ring: this wave's loads older than its
 // N most recent have landed in LDS and its own LDS reads have completed, then
 // every wave meets.  __syncthreads() would add a workgroup fence, which also
@@ -905,6 +920,12 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
       // 32x32 path (one long K loop per tile, C read after it); on smaller
       // tiles the one-at-a-time tail it needs costs more than it saves.
       constexpr bool kCPrefetch = VEC && S == 2 && L::PATH == kPathMfma32 && lg.BM * lg.BN >= 256 * 256;
+      // MFMAs per k-group and the wave's direct-to-LDS loads per slice:
+      // where the group after the barrier has two MFMAs or more per load,
+      // the loads are spread over it.
+      constexpr int kMf = 4 * lg.WMITER * lg.WNITER;
+      constexpr int kVm = dma_ops_a(lg, VEC ? 4 : 1) + dma_ops_b(lg, VEC ? 4 : 1);
+      constexpr bool kSpread = kMf >= 2 * kVm;
       DmaFrag<L> f[2];
       dma_frag_load<L>(lds + ro, 0, wr0, wc0, lane, f[0]);
       dma_slice<L, VEC>(p, d, lds + ro + (S - 1) * lg.STAGE, slice_k0(kt0 + S - 1, r, lg.BK), wave);
@@ -942,6 +963,7 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
           dma_slice<L, VEC>(p, d, lds + ro + cs * lg.STAGE, slice_k0(kt + S, r, lg.BK), wave);
         }
         dma_frag_mfma<L>(f[(KG - 1) & 1], acc);
+        if constexpr (kSpread) spread_loads<kMf, kVm>();
         if constexpr ((KG & 1) != 0) f[0] = f[1];
       };
       if constexpr (S == 2 && VEC && kCPrefetch) {
