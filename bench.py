@@ -60,6 +60,21 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_each_way": 4 * n, "launches": 3}), flush=True)
 
 
+# The sources that make up the kernels' code (not the dispatch table):
+# traffic counters in profiles/traffic.json count only for the kernel code
+# they were taken on.
+KERNEL_SOURCES = ("sgemm_kernels.hpp", "tile_maps.hpp", "tile_config.hpp", "registry.hpp")
+
+
+def kernel_fingerprint():
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "fp32_gemm_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -300,7 +315,7 @@ def main():
         with open(tpath) as f:
             tr = json.load(f)
         key = f"{args.workload}:{'/'.join(map(str, info['tuple']))}"
-        if key in tr:
+        if key in tr and tr[key].get("kernel") == kernel_fingerprint():
             traffic = tr[key]["bytes_per_launch"]
 
     out = {

@@ -170,10 +170,10 @@ def write_summary(best_by_shape_path, path, command, finalists=6):
 
 def retime(names, shapes, dev, results_path, top, summary_path, command):
     """Interleaved re-timing, per shape, of the tuned dispatch's choice and the
-    `top` fastest matrix-core tuples of a previous sweep (short protocol
-    records in `results_path`): 20 warm-up launches each, then rounds of one
+    `top` fastest matrix-core tuples of previous sweeps (short protocol
+    records in `results_path`, comma-separated files): 20 warm-up launches each, then rounds of one
     5-launch batch of each in turn (30 rounds; 12 above 2 * 4096^3 FLOP)."""
-    recs = [json.loads(l) for l in open(results_path)]
+    recs = [json.loads(l) for path in results_path.split(",") for l in open(path)]
     ids = {c["tuple"]: c["id"] for c in fg.configs()}
     stream = torch.cuda.current_stream(dev)
     lines = ["# Tuned-table rules: interleaved re-timing against each shape's best sweep candidates", "",
@@ -271,7 +271,8 @@ def main():
                          "sweep's short timings are noisier than the gaps between the best tuples")
     ap.add_argument("--retime", default=None,
                     help="re-time, per shape in --workloads, the tuned dispatch's choice against the "
-                         "--top fastest matrix-core tuples of this results file (no sweep)")
+                         "--top fastest matrix-core tuples of these results files (comma-separated; "
+                         "no sweep)")
     ap.add_argument("--best", default=None,
                     help="print the best tuple recorded for this workload in --out and exit")
     args = ap.parse_args()
