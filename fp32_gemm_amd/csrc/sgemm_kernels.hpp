@@ -917,9 +917,13 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
       // (dma_c_band).
       constexpr int KG = lg.BK / dma_kgroup(lg);
       // The C prefetch of the last slices pays on the 256x256 tiles of the
-      // 32x32 path (one long K loop per tile, C read after it); on smaller
-      // tiles the one-at-a-time tail it needs costs more than it saves.
-      constexpr bool kCPrefetch = VEC && S == 2 && L::PATH == kPathMfma32 && lg.BM * lg.BN >= 256 * 256;
+      // 32x32 path and on the 128x128 tiles of both paths (one long K loop
+      // per tile, C read after it, most of all when C is not in the caches);
+      // on 64-row tiles the one-at-a-time tail it needs costs more than it
+      // saves.
+      constexpr bool kCPrefetch = VEC && S == 2 &&
+                                  ((L::PATH == kPathMfma32 && lg.BM * lg.BN >= 256 * 256) ||
+                                   lg.BM * lg.BN == 128 * 128);
       // MFMAs per k-group and the wave's direct-to-LDS loads per slice:
       // where the group after the barrier has two MFMAs or more per load,
       // the loads are spread over it.
