@@ -276,9 +276,12 @@ __device__ __forceinline__ void dma_slice(const KernelArgs& p, const DmaLanes<Cf
 }
 
 // Past the K segment the ring has nothing left to fetch: the last slices'
-// loads bring band `band` (32-row bands, float4 variant) of this wave's C
-// tile into the caches instead, through the freed stage (never read), so the
-// epilogue's first reads of C hit.  With beta == 0 the resource is empty.
+// loads bring band `band` of this wave's C tile into the caches instead,
+// through the freed stage (never read), so the epilogue's first reads of C
+// hit.  A band is as many rows as one slice's loads cover in float4s (with
+// eight loads per wave, 32 rows of a 64-wide wave tile or 64 rows of a
+// 32-wide one); rows past the wave tile are masked.  With beta == 0 the
+// resource is empty.
 template <class Cfg>
 __device__ __forceinline__ void dma_c_band(const KernelArgs& p, float* stage, int crow0, int ccol0,
                                            int band, int wave, int lane) {
@@ -912,9 +915,8 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
       // have nearly S-1 slices to land.  The last iteration reads one group
       // of the stage past the segment, which is never multiplied; the last S
       // slices have no slice left to load, and load either nothing (zeros
-      // past K) or, on the 32x32 path's 256x256 tiles in the float4 variant,
-      // bands of the wave's C tile that the epilogue reads first
-      // (dma_c_band).
+      // past K) or, on the tiles named below in the float4 variant, bands of
+      // the wave's C tile that the epilogue reads first (dma_c_band).
       constexpr int KG = lg.BK / dma_kgroup(lg);
       // The C prefetch of the last slices pays on the 256x256 tiles of the
       // 32x32 path and on the 128x128 tiles of both paths (one long K loop
