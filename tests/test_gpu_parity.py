@@ -328,6 +328,49 @@ def test_integer_inputs_bit_exact_full_size(fg, dev, orc, shape):
     assert np.array_equal(cv.result().view(np.uint32), want.view(np.uint32))
 
 
+def test_random_shapes_tuned_dispatch(fg, dev, orc):
+    """Seeded shapes off every table (half with M, N, K log-uniform in
+    [1, 2500], mostly thin; half uniform in [200, 2500]),
+    random alpha / beta (beta = 0 on a quarter of them), A and B inside
+    NaN-filled buffers with padded leading dimensions, C inside canaries:
+    the tuned dispatch must meet the parity bar on every output, and on
+    integer-valued inputs, with alpha and beta that keep every product and
+    sum exact in fp32, match the oracle bit for bit."""
+    rng = np.random.default_rng(2024)
+    for case in range(24):
+        if case % 2 == 0:
+            M, N, K = (int(round(np.exp(rng.uniform(0, np.log(2500))))) for _ in range(3))
+        else:
+            M, N, K = (int(x) for x in rng.integers(200, 2501, 3))
+        alpha = float(np.float32(rng.uniform(-2, 2)))
+        beta = 0.0 if case % 4 == 3 else float(np.float32(rng.uniform(-2, 2)))
+        pa, pb, pc = (int(x) for x in rng.integers(0, 8, 3))
+        log(f"[random] case {case}: {M}x{N}x{K} alpha={alpha:.4f} beta={beta:.4f} pads {pa},{pb},{pc}")
+        for ints in (False, True):
+            a, b = alpha, beta
+            if ints:
+                A, B, C = inputs.make_small_int(M, N, K, seed=3000 + case)
+                a = (0.5, -1.0, 2.0, 0.25)[case % 4]
+                b = (3.0, -1.5, 0.5, 0.0)[case % 4]
+            else:
+                A, B, C = inputs.make_random(M, N, K, seed=3000 + case)
+            want32, want64 = orc.sgemm(A, B, C, a, b)
+            Abig = torch.full((M, K + pa), float("nan"), device=dev)
+            Bbig = torch.full((K, N + pb), float("nan"), device=dev)
+            Abig[:, :K] = to_dev(A, dev)
+            Bbig[:, :N] = to_dev(B, dev)
+            cv = Canvas(C, N + pc, 2, dev)
+            fg.sgemm_ex(Abig[:, :K], Bbig[:, :N], cv.view, a, b)
+            torch.cuda.synchronize()
+            assert cv.untouched(), f"case {case}: wrote outside C"
+            got = cv.result()
+            if ints:
+                assert np.array_equal(got.view(np.uint32), want32.view(np.uint32)), \
+                    f"case {case}: integer inputs not bit-exact"
+            else:
+                check_close(got, want64, K, A, B, f"case {case} {M}x{N}x{K}")
+
+
 def test_zero_operand_exact(fg, dev, orc):
     # An all-zero A makes the parity scale zero: the result must then equal
     # the oracle's correctly rounded beta * C exactly.
