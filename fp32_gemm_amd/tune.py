@@ -12,12 +12,15 @@ loop with a shorter warm-up for the sweep than for the final benchmark.
 
     python -m fp32_gemm_amd.tune [--workloads a,b] [--out results.jsonl]
                                  [--table-out tuned_table.inc]
+    python -m fp32_gemm_amd.tune --workloads a,b --retime results.jsonl[,more.jsonl]
+                                 [--top 5] [--table-out tuned_table.inc]
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -182,6 +185,7 @@ def retime(names, shapes, dev, results_path, top, summary_path, command):
              "sweep in the results file, 20 warm-up launches each, then rounds of one 5-launch batch of "
              "each in turn (30 rounds; 12 at 8192^3), on the workload's own inputs; medians in TFLOP/s.", "",
              "| shape | tuple (BM,BN,BK,WM,WN,WNITER,TM,TN,NT,path,swz,opt) | TFLOP/s |", "|---|---|---|"]
+    results = {}
     for name in names:
         w = shapes[name]
         A, B, C = inputs.make(w)
@@ -212,6 +216,7 @@ def retime(names, shapes, dev, results_path, top, summary_path, command):
                 samples[i].append(e0.elapsed_time(e1) / 5)
         rows = sorted(((flops / (float(np.median(v)) * 1e-3) / 1e12, t) for t, v in zip(cands, samples)),
                       reverse=True)
+        results[(w.M, w.N, w.K)] = (chosen_t, rows)
         for tf, t in rows:
             mark = " *" if t == chosen_t else ""
             lines.append(f"| {name} | {','.join(str(x) for x in t)}{mark} | {tf:.2f} |")
@@ -219,6 +224,37 @@ def retime(names, shapes, dev, results_path, top, summary_path, command):
     if summary_path:
         with open(summary_path, "w") as f:
             f.write("\n".join(lines) + "\n")
+    return results
+
+
+_RULE = re.compile(r"^(\s*)\{(\d+), (\d+), (\d+), \{([-\d, ]+)\}\},\s*// ([^:]*):.*$")
+
+
+def update_table(path, results, lead=0.01):
+    """Rewrites the rules of the re-timed shapes in an existing table: a rule
+    moves to the fastest re-timed tuple only where that tuple leads the
+    rule's own by more than `lead` (the re-timing's spread between runs is
+    about 1 %); every rule re-timed gets its measured rate in its comment.
+    Rules of other shapes and the default tiles are left as they are."""
+    out, changed = [], []
+    with open(path) as f:
+        text = f.read()
+    for line in text.split("\n"):
+        m = _RULE.match(line)
+        key = tuple(int(m.group(i)) for i in (2, 3, 4)) if m else None
+        if key in results:
+            chosen, rows = results[key]
+            rate = {t: tf for tf, t in rows}
+            best_tf, best = rows[0]
+            pick = best if best_tf > rate[chosen] * (1 + lead) else chosen
+            if pick != chosen:
+                changed.append((key, chosen, pick))
+            line = "%s{%d, %d, %d, {%s}},  // %s: %.1f TFLOP/s (re-timed)" % (
+                m.group(1), *key, ", ".join(str(x) for x in pick), m.group(6), rate[pick])
+        out.append(line)
+    with open(path, "w") as f:
+        f.write("\n".join(out))
+    return changed
 
 
 def write_table(best_by_shape, path, defaults):
@@ -250,7 +286,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--workloads", default=",".join(list(inputs.WORKLOADS) + list(inputs.TUNING_EXTRA)))
     ap.add_argument("--out", default="tune_results.jsonl")
-    ap.add_argument("--table-out", default=None)
+    ap.add_argument("--table-out", default=None,
+                    help="write the dispatch table from the sweep; with --retime, update the "
+                         "re-timed shapes' rules in this existing table instead")
     ap.add_argument("--paths", default="valu,mfma32,mfma16")
     ap.add_argument("--prune-above", type=float, default=float("inf"),
                     help="shapes with more FLOP than this only try the best --keep configs per "
@@ -287,8 +325,11 @@ def main():
         raise SystemExit("tune: current device is not gfx950")
     if args.retime:
         shapes = {**inputs.WORKLOADS, **inputs.TUNING_EXTRA}
-        retime(args.workloads.split(","), shapes, dev, args.retime, args.top, args.summary_out,
-               "python -m fp32_gemm_amd.tune " + " ".join(sys.argv[1:]))
+        results = retime(args.workloads.split(","), shapes, dev, args.retime, args.top,
+                         args.summary_out, "python -m fp32_gemm_amd.tune " + " ".join(sys.argv[1:]))
+        if args.table_out:
+            for key, old_t, new_t in update_table(args.table_out, results):
+                print(f"[retime] rule {key}: {old_t} -> {new_t}", flush=True)
         return 0
     paths = set(args.paths.split(","))
     configs = {v: [c for c in usable_configs(v) if c["path_name"] in paths] for v in (True, False)}
