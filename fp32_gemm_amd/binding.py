@@ -204,22 +204,41 @@ def plan(M, N, K, A_ptr, lda, B_ptr, ldb, C_ptr, ldc, cfg_id=-1) -> dict:
 
 
 def _operand(t, name):
+    """(data pointer, leading dimension) of a 2-D float32 GPU tensor with unit
+    column stride; raises on anything else."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.dtype != torch.float32:
+    if t.dtype is not torch.float32:
         raise TypeError(f"{name} must be float32, got {t.dtype}")
-    if t.dim() != 2:
+    shape = t.shape
+    if len(shape) != 2:
         raise ValueError(f"{name} must be 2-D")
-    if t.shape[1] > 1 and t.stride(1) != 1:
+    rows, cols = shape
+    s0, s1 = t.stride()
+    if cols > 1 and s1 != 1:
         raise ValueError(f"{name} must have unit column stride (row-major)")
-    if t.shape[0] > 1 and t.shape[1] > 0 and t.stride(0) < t.shape[1]:
+    if rows > 1 and cols > 0 and s0 < cols:
         # Expanded or otherwise overlapping rows: no leading dimension
         # describes them, and the kernels would read past the storage.
-        raise ValueError(f"{name}: rows overlap (row stride {t.stride(0)} < {t.shape[1]} columns)")
-    if t.device.type != "cuda":
+        raise ValueError(f"{name}: rows overlap (row stride {s0} < {cols} columns)")
+    if not t.is_cuda:
         raise ValueError(f"{name} must be on a GPU device")
-    ld = t.stride(0) if t.shape[0] > 1 else t.shape[1]
-    return t.data_ptr(), max(ld, 1)
+    ld = s0 if rows > 1 else cols
+    return t.data_ptr(), (ld if ld > 1 else 1)
+
+
+# The raw handle of torch's current stream on a device, without building a
+# Stream object (which costs more than the rest of a call); the public route
+# where this build of torch lacks it.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream_handle(dev, stream):
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    if _raw_stream is not None:
+        return _raw_stream(dev.index if dev.index is not None else torch.cuda.current_device())
+    return torch.cuda.current_stream(dev).cuda_stream
 
 
 def sgemm_ex(A, B, C, alpha=1.0, beta=0.0, stream=None, cfg_id=-1):
@@ -235,15 +254,13 @@ def sgemm_ex(A, B, C, alpha=1.0, beta=0.0, stream=None, cfg_id=-1):
     c, ldc = _operand(C, "C")
     M, K = A.shape
     K2, N = B.shape
-    if K2 != K or tuple(C.shape) != (M, N):
+    if K2 != K or C.shape != (M, N):
         raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, C {tuple(C.shape)}")
-    if not (A.device == B.device == C.device):
-        raise ValueError("A, B and C must be on the same device")
     dev = C.device
-    if stream is None:
-        stream = torch.cuda.current_stream(dev)
-    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
-    if dev.index == torch.cuda.current_device():
+    if A.device != dev or B.device != dev:
+        raise ValueError("A, B and C must be on the same device")
+    handle = _stream_handle(dev, stream)
+    if dev.index is None or dev.index == torch.cuda.current_device():
         rc = _lib.sgemm_ex(M, N, K, alpha, a, lda, b, ldb, beta, c, ldc, handle, cfg_id)
     else:
         with torch.cuda.device(dev):
