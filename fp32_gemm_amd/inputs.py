@@ -71,6 +71,19 @@ TUNING_EXTRA = {
         Workload("shortk4096x4096x16", 4096, 4096, 16, "uniform", "uniform", 0.5, 3.0, 15),
         Workload("shortk8192x8192x32", 8192, 8192, 32, "uniform", "uniform", 0.5, 3.0, 16),
         Workload("deepk1024x1024x65536", 1024, 1024, 65536, "uniform", "uniform", 0.5, 3.0, 17),
+        # Odd extents: K or N not a multiple of 4, so these run the scalar
+        # variant (4-byte operand loads), whose best tiles differ from the
+        # aligned shapes'; other odd shapes take their rules.
+        Workload("odd1025x1023x1021", 1025, 1023, 1021, "uniform", "uniform", 0.5, 3.0, 18),
+        Workload("odd2049x2047x2045", 2049, 2047, 2045, "uniform", "uniform", 0.5, 3.0, 19),
+        Workload("odd3073x3071x3069", 3073, 3071, 3069, "uniform", "uniform", 0.5, 3.0, 20),
+        Workload("odd6145x6143x6141", 6145, 6143, 6141, "uniform", "uniform", 0.5, 3.0, 21),
+        Workload("odd1025x8191x321", 1025, 8191, 321, "uniform", "uniform", 0.5, 3.0, 22),
+        Workload("odd8191x1025x321", 8191, 1025, 321, "uniform", "uniform", 0.5, 3.0, 23),
+        Workload("odd4097x4095x513", 4097, 4095, 513, "uniform", "uniform", 0.5, 3.0, 24),
+        Workload("odd1025x1023x8191", 1025, 1023, 8191, "uniform", "uniform", 0.5, 3.0, 25),
+        Workload("odd2049x6143x1021", 2049, 6143, 1021, "uniform", "uniform", 0.5, 3.0, 26),
+        Workload("odd6145x2047x3069", 6145, 2047, 3069, "uniform", "uniform", 0.5, 3.0, 27),
     ]
 }
 

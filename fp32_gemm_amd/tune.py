@@ -216,7 +216,7 @@ def retime(names, shapes, dev, results_path, top, summary_path, command):
                 samples[i].append(e0.elapsed_time(e1) / 5)
         rows = sorted(((flops / (float(np.median(v)) * 1e-3) / 1e12, t) for t, v in zip(cands, samples)),
                       reverse=True)
-        results[(w.M, w.N, w.K)] = (chosen_t, rows)
+        results[(w.M, w.N, w.K)] = (chosen_t, rows, name)
         for tf, t in rows:
             mark = " *" if t == chosen_t else ""
             lines.append(f"| {name} | {','.join(str(x) for x in t)}{mark} | {tf:.2f} |")
@@ -230,20 +230,159 @@ def retime(names, shapes, dev, results_path, top, summary_path, command):
 _RULE = re.compile(r"^(\s*)\{(\d+), (\d+), (\d+), \{([-\d, ]+)\}\},\s*// ([^:]*):.*$")
 
 
+def off_table(seed, dev, out_path, summary_path, command, count=36):
+    """Dispatch study on seeded shapes that no rule was tuned on: a third
+    each with M, N, K uniform in [512, 8192], log-uniform in [256, 16384],
+    and M, N in [1024, 8192] with K in [64, 1024] (shapes above 8192^3's
+    work skipped).  Per shape the tuned dispatch's choice, the tuple of every
+    table rule and torch.mm are timed interleaved (3 warm-up launches each,
+    then 6 rounds of one 3-launch batch of each in turn; A, B normal, beta
+    = 0); the summary reports the dispatch's rate against the best rule's
+    and against torch.mm."""
+    rules = []
+    for line in open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc",
+                                  "tuned_table.inc")):
+        m = _RULE.match(line)
+        if m:
+            rules.append(tuple(int(x) for x in m.group(5).split(", ")))
+    ids = {c["tuple"]: c["id"] for c in fg.configs()}
+    rng = np.random.default_rng(seed)
+    stream = torch.cuda.current_stream(dev)
+    recs = []
+    for i in range(count):
+        if i % 3 == 0:
+            M, N, K = (int(x) for x in rng.integers(512, 8193, 3))
+        elif i % 3 == 1:
+            M, N, K = (int(round(np.exp(rng.uniform(np.log(256), np.log(16384))))) for _ in range(3))
+        else:
+            M, N = (int(x) for x in rng.integers(1024, 8193, 2))
+            K = int(rng.integers(64, 1025))
+        if 2 * M * N * K > 2 * 8192 ** 3:
+            continue
+        A = torch.randn(M, K, device=dev)
+        B = torch.randn(K, N, device=dev)
+        C = torch.randn(M, N, device=dev)
+        chosen = fg.plan(M, N, K, A.data_ptr(), K, B.data_ptr(), N, C.data_ptr(), N)["cfg_id"]
+        cands = sorted({ids[t] for t in rules if t in ids} | {chosen})
+        fns = {c: (lambda c=c: fg.sgemm_ex(A, B, C, 1.0, 0.0, stream=stream, cfg_id=c)) for c in cands}
+        Cm = torch.empty_like(C)
+        fns["torch.mm"] = lambda: torch.mm(A, B, out=Cm)
+        for f in fns.values():
+            for _ in range(3):
+                f()
+        samples = {k: [] for k in fns}
+        for _ in range(6):
+            for k, f in fns.items():
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(3):
+                    f()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                samples[k].append(e0.elapsed_time(e1) / 3)
+        rate = {k: model.flops(M, N, K) / (float(np.median(v)) * 1e-3) / 1e12 for k, v in samples.items()}
+        best = max(cands, key=lambda c: rate[c])
+        rec = dict(M=M, N=N, K=K, vec=bool(N % 4 == 0 and K % 4 == 0), chosen=fg.config_info(chosen)["tuple"],
+                   chosen_tflops=round(rate[chosen], 2), best=fg.config_info(best)["tuple"],
+                   best_tflops=round(rate[best], 2), torch_tflops=round(rate["torch.mm"], 2))
+        # Every candidate's rate and launch plan, so another selection policy
+        # can be scored against the same timings.
+        key = lambda c: ",".join(map(str, fg.config_info(c)["tuple"]))
+        rec["rates"] = {key(c): round(rate[c], 2) for c in cands}
+        rec["plans"] = {key(c): {k: v for k, v in fg.plan(M, N, K, A.data_ptr(), K, B.data_ptr(), N,
+                                                          C.data_ptr(), N, c).items()
+                                 if k in ("grid", "slots", "tiles_full", "splits")} for c in cands}
+        recs.append(rec)
+        print(f"[off-table] {M}x{N}x{K} dispatch {rec['chosen_tflops']:.1f}, best rule "
+              f"{rec['best_tflops']:.1f}, torch.mm {rec['torch_tflops']:.1f}", flush=True)
+    if out_path:
+        with open(out_path, "w") as f:
+            for r in recs:
+                f.write(json.dumps(r) + "\n")
+    if summary_path:
+        g = lambda xs: float(np.exp(np.mean(np.log(xs))))
+        of_best = [r["chosen_tflops"] / r["best_tflops"] for r in recs]
+        vs_torch = [r["chosen_tflops"] / r["torch_tflops"] for r in recs]
+        lines = [f"# Dispatch on seeded off-table shapes (seed {seed})", "", f"Command: `{command}`", "",
+                 off_table.__doc__.split("\n\n")[0].replace("\n    ", " ").strip(), "",
+                 f"{len(recs)} shapes ({sum(not r['vec'] for r in recs)} scalar-variant). The dispatch's "
+                 f"choice reaches {g(of_best):.3f} of the best table rule's rate (geometric mean; worst "
+                 f"{min(of_best):.3f}) and {g(vs_torch):.3f}x torch.mm (worst {min(vs_torch):.3f}x).", "",
+                 "| M | N | K | variant | dispatch tuple | TFLOP/s | best rule tuple | TFLOP/s | torch.mm |",
+                 "|---|---|---|---|---|---|---|---|---|"]
+        for r in recs:
+            lines.append(f"| {r['M']} | {r['N']} | {r['K']} | {'float4' if r['vec'] else 'scalar'} | "
+                         f"{','.join(map(str, r['chosen']))} | {r['chosen_tflops']:.1f} | "
+                         f"{','.join(map(str, r['best']))} | {r['best_tflops']:.1f} | {r['torch_tflops']:.1f} |")
+        with open(summary_path, "w") as f:
+            f.write("\n".join(lines) + "\n")
+    return recs
+
+
+def write_rate_table(records, path, command):
+    """The measured-rate table that the dispatch consults for scalar-variant
+    shapes: one row per scalar-variant shape of the off-table studies'
+    records, with each column tile's rate as a percentage (at least 1) of the
+    row's fastest column.  The columns are the tuples timed on every such
+    shape.  A shape measured twice keeps its first record."""
+    rows, seen = [], set()
+    for r in records:
+        key = (r["M"], r["N"], r["K"])
+        if r["vec"] or key in seen:
+            continue
+        seen.add(key)
+        rows.append(r)
+    if not rows:
+        raise ValueError("no scalar-variant records with rates")
+    common = set(rows[0]["rates"])
+    for r in rows[1:]:
+        common &= set(r["rates"])
+    cols = sorted(common, key=lambda t: tuple(int(x) for x in t.split(",")))
+    lines = [
+        "// scalar_rates.inc -- measured-rate table for scalar-variant shapes.",
+        "//",
+        f"// Written by `{command}`",
+        "// from off-table dispatch studies (tune.py --off-table): each row is a",
+        "// seeded shape that runs the scalar variant, with every column tile's",
+        "// rate there as a percentage of the row's fastest column (at least 1).",
+        "// select_config in sgemm_api.hip describes how the dispatch reads it.",
+        "// Tile order: {BM, BN, BK, WM, WN, WNITER, TM, TN, NT, path, swz, opt}.",
+        "",
+        "static constexpr Tile kRateTiles[] = {",
+    ]
+    for i, t in enumerate(cols):
+        lines.append("    {%s},  // column %d" % (t.replace(",", ", "), i))
+    lines += ["};", "", "static const RateRow kRateRows[] = {"]
+    for r in sorted(rows, key=lambda r: (r["M"], r["N"], r["K"])):
+        best = max(r["rates"][t] for t in cols)
+        pct = [max(1, int(round(100.0 * r["rates"][t] / best))) for t in cols]
+        lines.append("    {%d, %d, %d, {%s}},  // best %.1f TFLOP/s" % (
+            r["M"], r["N"], r["K"], ", ".join(map(str, pct)), best))
+    lines += ["};", ""]
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+    return cols, len(rows)
+
+
 def update_table(path, results, lead=0.01):
     """Rewrites the rules of the re-timed shapes in an existing table: a rule
     moves to the fastest re-timed tuple only where that tuple leads the
     rule's own by more than `lead` (the re-timing's spread between runs is
     about 1 %); every rule re-timed gets its measured rate in its comment.
-    Rules of other shapes and the default tiles are left as they are."""
-    out, changed = [], []
+    A re-timed shape without a rule gets one, with its fastest tuple, at the
+    end of the table.  Rules of other shapes and the default tiles are left
+    as they are."""
+    out, changed, seen = [], [], set()
+    in_rules = False
     with open(path) as f:
         text = f.read()
     for line in text.split("\n"):
         m = _RULE.match(line)
+        in_rules = in_rules or m is not None
         key = tuple(int(m.group(i)) for i in (2, 3, 4)) if m else None
         if key in results:
-            chosen, rows = results[key]
+            seen.add(key)
+            chosen, rows = results[key][:2]
             rate = {t: tf for tf, t in rows}
             best_tf, best = rows[0]
             pick = best if best_tf > rate[chosen] * (1 + lead) else chosen
@@ -251,6 +390,16 @@ def update_table(path, results, lead=0.01):
                 changed.append((key, chosen, pick))
             line = "%s{%d, %d, %d, {%s}},  // %s: %.1f TFLOP/s (re-timed)" % (
                 m.group(1), *key, ", ".join(str(x) for x in pick), m.group(6), rate[pick])
+        if in_rules and line.startswith("};"):
+            in_rules = False
+            for key, (chosen, rows, name) in results.items():
+                if key in seen:
+                    continue
+                best_tf, best = rows[0]
+                out.append("    {%d, %d, %d, {%s}},  // %s (tuning only): %.1f TFLOP/s (re-timed)" % (
+                    *key, ", ".join(str(x) for x in best), name, best_tf))
+                changed.append((key, None, best))
+                seen.add(key)
         out.append(line)
     with open(path, "w") as f:
         f.write("\n".join(out))
@@ -262,8 +411,9 @@ def write_table(best_by_shape, path, defaults):
         "// tuned_table.inc -- dispatch table for the tuned choice of tile tuple.",
         "//",
         "// kTuned lists shapes with the tuple the autotuner measured fastest on",
-        "// them (fp32_gemm_amd/tune.py); other shapes take the tuned rule nearest in",
-        "// log(M), log(N), log(K).  Tuple order:",
+        "// them (fp32_gemm_amd/tune.py); other shapes choose among the rules, or",
+        "// from the measured-rate table of scalar_rates.inc, as select_config in",
+        "// sgemm_api.hip describes.  Tuple order:",
         "// {BM, BN, BK, WM, WN, WNITER, TM, TN, NT, path, swz, opt}.",
         "",
         "static const TunedRule kTuned[] = {",
@@ -313,7 +463,24 @@ def main():
                          "no sweep)")
     ap.add_argument("--best", default=None,
                     help="print the best tuple recorded for this workload in --out and exit")
+    ap.add_argument("--off-table", type=int, default=None, metavar="SEED",
+                    help="dispatch study on seeded shapes off the table (writes --out and "
+                         "--summary-out), no sweep")
+    ap.add_argument("--rate-table", default=None, metavar="FILES",
+                    help="write --rate-table-out from these off-table records (comma-separated "
+                         "JSONL files of --off-table runs); no GPU needed")
+    ap.add_argument("--rate-table-out", default=None)
     args = ap.parse_args()
+    if args.rate_table:
+        recs = [json.loads(l) for f in args.rate_table.split(",") for l in open(f) if l.strip()]
+        # The command as written into the table names the record files
+        # without their directory.
+        names = ",".join(os.path.basename(f) for f in args.rate_table.split(","))
+        cols, n = write_rate_table(recs, args.rate_table_out,
+                                   f"python -m fp32_gemm_amd.tune --rate-table {names} "
+                                   f"--rate-table-out {args.rate_table_out}")
+        print(f"[rate-table] {n} rows x {len(cols)} columns -> {args.rate_table_out}")
+        return 0
     if args.best:
         recs = [json.loads(l) for l in open(args.out)]
         fin = [r for r in recs if r["workload"] == args.best and r.get("protocol") == "long"]
@@ -323,6 +490,10 @@ def main():
     torch.cuda.set_device(dev)
     if fg.device_check() != 0:
         raise SystemExit("tune: current device is not gfx950")
+    if args.off_table is not None:
+        off_table(args.off_table, dev, args.out, args.summary_out,
+                  "python -m fp32_gemm_amd.tune " + " ".join(sys.argv[1:]))
+        return 0
     if args.retime:
         shapes = {**inputs.WORKLOADS, **inputs.TUNING_EXTRA}
         results = retime(args.workloads.split(","), shapes, dev, args.retime, args.top,

@@ -1,6 +1,7 @@
 """The C ABI on the CPU: the library loads, exports every function the header
 declares, and validates arguments before touching any device."""
 import ctypes
+import math
 import os
 import re
 import subprocess
@@ -131,15 +132,14 @@ def test_off_table_rules_follow_the_variant():
     # Off the table, a shape takes a rule tuned on a shape of its own variant:
     # the ragged rules (tuned where only the 4-byte scalar variant runs) serve
     # unaligned shapes, the aligned rules aligned ones, even where a ragged
-    # rule's shape is nearer.  Without a device the nearest such rule is
-    # reported (the fill check needs the device's occupancy).
-    text = open(os.path.join(ROOT, "fp32_gemm_amd", "csrc", "tuned_table.inc")).read()
-    rules = {(int(M), int(N), int(K)): tuple(int(x) for x in t.split(","))
-             for M, N, K, t in re.findall(r"\{(\d+), (\d+), (\d+), \{([\d, ]+)\}\}", text)}
+    # rule's shape is nearer.  Without a device the fill check (it needs the
+    # device's occupancy) counts every launch as full, and the nearest such
+    # rule is reported.  (Unaligned shapes inside the measured-rate table's
+    # range choose from that table instead: the next test.)
+    rules = _table_rules()
     import torch
     if torch.cuda.is_available():
         pytest.skip("the fill check changes the choice on a device")
-    import math
 
     def nearest(M, N, K, aligned):
         d = {s: sum(math.log2(a / b) ** 2 for a, b in zip((M, N, K), s))
@@ -154,9 +154,72 @@ def test_off_table_rules_follow_the_variant():
     assert code == 0 and p["vector_variant"] == 1
     assert tuple(fg.config_info(p["cfg_id"])["tuple"]) == nearest(12288, 12288, 1024, True)
     assert tuple(fg.config_info(p["cfg_id"])["tuple"]) != rules[(4097, 4095, 4093)]
-    code, p = plan(4000, 4001, 4003, 4003, 4001, 4001)
-    assert code == 0 and p["vector_variant"] == 0
-    assert tuple(fg.config_info(p["cfg_id"])["tuple"]) == nearest(4000, 4001, 4003, False)
+    for M, N, K in ((100, 3001, 2999), (5000, 64, 777), (3000, 3001, 20)):
+        code, p = plan(M, N, K, K, N, N)
+        assert code == 0 and p["vector_variant"] == 0
+        assert tuple(fg.config_info(p["cfg_id"])["tuple"]) == nearest(M, N, K, False), (M, N, K)
+
+
+def _table_rules():
+    text = open(os.path.join(ROOT, "fp32_gemm_amd", "csrc", "tuned_table.inc")).read()
+    return {(int(M), int(N), int(K)): tuple(int(x) for x in t.split(","))
+            for M, N, K, t in re.findall(r"\{(\d+), (\d+), (\d+), \{([\d, ]+)\}\}", text)}
+
+
+def _rate_table():
+    text = open(os.path.join(ROOT, "fp32_gemm_amd", "csrc", "scalar_rates.inc")).read()
+    tiles_text = text[text.index("kRateTiles[]"):text.index("kRateRows[]")]
+    cols = [tuple(int(x) for x in t.split(",")) for t in re.findall(r"\{([\d, ]+)\},\s*// column", tiles_text)]
+    rows = [((int(M), int(N), int(K)), [int(x) for x in pct.split(",")])
+            for M, N, K, pct in re.findall(r"\{(\d+), (\d+), (\d+), \{([\d, ]+)\}\}",
+                                           text[text.index("kRateRows[]"):])]
+    return cols, rows
+
+
+def test_rate_table_is_well_formed():
+    # Every column names a compiled tuple; every row is a distinct shape that
+    # runs the scalar variant, holds one percentage per column, and has its
+    # fastest column at 100.
+    cols, rows = _rate_table()
+    compiled = {tuple(c["tuple"]) for c in fg.configs()}
+    assert cols and rows and len(cols) <= 32
+    assert all(c in compiled for c in cols)
+    assert len({s for s, _ in rows}) == len(rows)
+    for (M, N, K), pct in rows:
+        assert not (N % 4 == 0 and K % 4 == 0), (M, N, K)
+        assert len(pct) == len(cols) and max(pct) == 100 and min(pct) >= 1
+
+
+def test_scalar_shapes_follow_the_rate_table():
+    # An unaligned shape without an exact rule, with M, N >= 128 and K >= 32,
+    # takes the column with the highest sum over the 16 nearest rows (in
+    # log2 M, log2 N and log2 K, the K difference weighing one half) of
+    # exp(-squared distance) * log(percentage / 100).  The choice needs no
+    # device, so this holds on any host.
+    cols, rows = _rate_table()
+    rules = _table_rules()
+
+    def expected(M, N, K):
+        x = (math.log2(M), math.log2(N), math.log2(K))
+        d = sorted(((x[0] - math.log2(s[0])) ** 2 + (x[1] - math.log2(s[1])) ** 2 +
+                    0.5 * (x[2] - math.log2(s[2])) ** 2, i) for i, (s, _) in enumerate(rows))[:16]
+        score = [sum(math.exp(-dd) * math.log(rows[i][1][c] / 100.0) for dd, i in d)
+                 for c in range(len(cols))]
+        return cols[max(range(len(cols)), key=lambda c: score[c])]
+
+    shapes = [(4000, 4001, 4003), (3603, 2045, 218), (1269, 7747, 321), (706, 1029, 963),
+              (128, 129, 32), (20001, 300, 5001), (1000, 1000, 1001)]
+    shapes += [s for s, _ in rows[:3]]   # a row's own shape
+    for M, N, K in shapes:
+        assert (M, N, K) not in rules
+        code, p = plan(M, N, K, K, N, N)
+        assert code == 0 and p["vector_variant"] == 0
+        assert tuple(fg.config_info(p["cfg_id"])["tuple"]) == expected(M, N, K), (M, N, K)
+    # An exact rule still wins over the table.
+    for s, t in rules.items():
+        if not (s[1] % 4 == 0 and s[2] % 4 == 0):
+            code, p = plan(*s, s[2], s[1], s[1])
+            assert tuple(fg.config_info(p["cfg_id"])["tuple"]) == t
 
 
 def test_quick_return_and_no_device():

@@ -24,17 +24,45 @@ def test_update_moves_only_rules_with_a_clear_lead(tmp_path):
     (k1, (t1, _)), (k2, (t2, _)) = list(before.items())[:2]
     other = (64, 128, 32, 64, 32, 1, 16, 1, 256, 1, 32, 24)
     assert other not in (t1, t2)
+    new_key = (3001, 2999, 997)
+    assert new_key not in before
     results = {
-        k1: (t1, [(102.0, other), (100.0, t1)]),     # leads by 2 %: the rule moves
-        k2: (t2, [(100.5, other), (100.0, t2)]),     # 0.5 %: the rule stays
+        k1: (t1, [(102.0, other), (100.0, t1)], "a"),     # leads by 2 %: the rule moves
+        k2: (t2, [(100.5, other), (100.0, t2)], "b"),     # 0.5 %: the rule stays
+        new_key: (t2, [(90.0, other), (88.0, t2)], "odd3001"),  # no rule yet: added
     }
     changed = tune.update_table(str(path), results)
     after = _rules(path)
-    assert changed == [(k1, t1, other)]
+    assert changed == [(k1, t1, other), (new_key, None, other)]
+    assert after[new_key][0] == other and "odd3001 (tuning only): 90.0" in after[new_key][1]
+    assert f"{{{', '.join(map(str, other))}}}}}," in after[new_key][1]
+    assert len(after) == len(before) + 1
     assert after[k1][0] == other and "102.0 TFLOP/s (re-timed)" in after[k1][1]
     assert after[k2][0] == t2 and "100.0 TFLOP/s (re-timed)" in after[k2][1]
     for k in before:
         if k not in (k1, k2):
             assert after[k] == before[k]
     text = path.read_text()
-    assert "kDefaultLarge" in text and text.count("{") == open(TABLE).read().count("{")
+    assert "kDefaultLarge" in text and text.count("{") == open(TABLE).read().count("{") + 2
+
+
+def test_rate_table_rows_and_columns(tmp_path):
+    # Scalar-variant records only, each shape once (the first record), the
+    # columns the tuples timed on every row, percentages of the row's best
+    # rounded and floored at 1.
+    a, b, c = "64,64,16,32,32,1,16,1,256,1,32,18", "128,128,16,64,64,4,4,1,256,2,64,24", \
+        "256,256,32,128,64,2,16,1,512,1,32,27"
+    recs = [
+        dict(M=1000, N=1001, K=999, vec=False, rates={a: 50.0, b: 100.0, c: 0.4}),
+        dict(M=300, N=301, K=302, vec=False, rates={a: 80.0, b: 40.0}),
+        dict(M=1000, N=1001, K=999, vec=False, rates={a: 100.0, b: 10.0}),   # repeat: ignored
+        dict(M=512, N=512, K=512, vec=True, rates={a: 1.0, b: 2.0}),         # float4: ignored
+    ]
+    path = tmp_path / "rates.inc"
+    cols, n = tune.write_rate_table(recs, str(path), "cmd")
+    assert cols == [a, b] and n == 2
+    text = path.read_text()
+    assert "{64, 64, 16, 32, 32, 1, 16, 1, 256, 1, 32, 18},  // column 0" in text
+    assert "{300, 301, 302, {100, 50}}" in text and "{1000, 1001, 999, {50, 100}}" in text
+    assert text.index("{300, 301, 302") < text.index("{1000, 1001, 999")
+    assert "512, 512, 512" not in text and "`cmd`" in text
