@@ -230,15 +230,22 @@ def retime(names, shapes, dev, results_path, top, summary_path, command):
 _RULE = re.compile(r"^(\s*)\{(\d+), (\d+), (\d+), \{([-\d, ]+)\}\},\s*// ([^:]*):.*$")
 
 
-def off_table(seed, dev, out_path, summary_path, command, count=36):
-    """Dispatch study on seeded shapes that no rule was tuned on: a third
-    each with M, N, K uniform in [512, 8192], log-uniform in [256, 16384],
-    and M, N in [1024, 8192] with K in [64, 1024] (shapes above 8192^3's
-    work skipped).  Per shape the tuned dispatch's choice, the tuple of every
+def off_table(seed, dev, out_path, summary_path, command, count=36, aligned=False, shapes=None,
+              mix="standard"):
+    """Dispatch study on seeded shapes that no rule was tuned on.  The
+    standard mix: a third each with M, N, K uniform in [512, 8192],
+    log-uniform in [256, 16384], and M, N in [1024, 8192] with K in
+    [64, 1024] (shapes above 8192^3's work skipped).  The large mix, all
+    log-uniform: a third each with M, N, K in [4096, 16384], M, N in
+    [4096, 16384] with K in [16, 512], and M, N in [2048, 16384] with K in
+    [8192, 65536] (shapes above 16384^3's work skipped).  With `aligned`, N
+    and K are rounded up to multiples of 4, so every shape runs the float4
+    variant.  Per shape the tuned dispatch's choice, the tuple of every
     table rule and torch.mm are timed interleaved (3 warm-up launches each,
     then 6 rounds of one 3-launch batch of each in turn; A, B normal, beta
     = 0); the summary reports the dispatch's rate against the best rule's
-    and against torch.mm."""
+    and against torch.mm.  `shapes`, a list of (M, N, K), replaces the
+    seeded shapes."""
     rules = []
     for line in open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc",
                                   "tuned_table.inc")):
@@ -249,15 +256,30 @@ def off_table(seed, dev, out_path, summary_path, command, count=36):
     rng = np.random.default_rng(seed)
     stream = torch.cuda.current_stream(dev)
     recs = []
-    for i in range(count):
-        if i % 3 == 0:
+    def log_uniform(lo, hi):
+        return int(round(np.exp(rng.uniform(np.log(lo), np.log(hi)))))
+
+    cap = 16384 ** 3 if mix == "large" else 8192 ** 3
+    for i in range(len(shapes) if shapes else count):
+        if shapes:
+            M, N, K = shapes[i]
+        elif mix == "large":
+            if i % 3 == 0:
+                M, N, K = (log_uniform(4096, 16384) for _ in range(3))
+            elif i % 3 == 1:
+                M, N, K = log_uniform(4096, 16384), log_uniform(4096, 16384), log_uniform(16, 512)
+            else:
+                M, N, K = log_uniform(2048, 16384), log_uniform(2048, 16384), log_uniform(8192, 65536)
+        elif i % 3 == 0:
             M, N, K = (int(x) for x in rng.integers(512, 8193, 3))
         elif i % 3 == 1:
-            M, N, K = (int(round(np.exp(rng.uniform(np.log(256), np.log(16384))))) for _ in range(3))
+            M, N, K = (log_uniform(256, 16384) for _ in range(3))
         else:
             M, N = (int(x) for x in rng.integers(1024, 8193, 2))
             K = int(rng.integers(64, 1025))
-        if 2 * M * N * K > 2 * 8192 ** 3:
+        if aligned:
+            N, K = -(-N // 4) * 4, -(-K // 4) * 4
+        if not shapes and M * N * K > cap:
             continue
         A = torch.randn(M, K, device=dev)
         B = torch.randn(K, N, device=dev)
@@ -303,7 +325,9 @@ def off_table(seed, dev, out_path, summary_path, command, count=36):
         g = lambda xs: float(np.exp(np.mean(np.log(xs))))
         of_best = [r["chosen_tflops"] / r["best_tflops"] for r in recs]
         vs_torch = [r["chosen_tflops"] / r["torch_tflops"] for r in recs]
-        lines = [f"# Dispatch on seeded off-table shapes (seed {seed})", "", f"Command: `{command}`", "",
+        kind = "aligned " if aligned else ""
+        title = "given shapes" if shapes else f"seeded {kind}off-table shapes ({mix} mix, seed {seed})"
+        lines = [f"# Dispatch on {title}", "", f"Command: `{command}`", "",
                  off_table.__doc__.split("\n\n")[0].replace("\n    ", " ").strip(), "",
                  f"{len(recs)} shapes ({sum(not r['vec'] for r in recs)} scalar-variant). The dispatch's "
                  f"choice reaches {g(of_best):.3f} of the best table rule's rate (geometric mean; worst "
@@ -320,48 +344,57 @@ def off_table(seed, dev, out_path, summary_path, command, count=36):
 
 
 def write_rate_table(records, path, command):
-    """The measured-rate table that the dispatch consults for scalar-variant
-    shapes: one row per scalar-variant shape of the off-table studies'
-    records, with each column tile's rate as a percentage (at least 1) of the
-    row's fastest column.  The columns are the tuples timed on every such
-    shape.  A shape measured twice keeps its first record."""
+    """The measured-rate table that the dispatch consults off the rules: per
+    variant, one row per shape of the off-table studies' records, with each
+    column tile's rate as a percentage (at least 1) of the row's fastest
+    column.  The columns are the tuples timed on every shape.  A shape
+    measured twice keeps its first record."""
     rows, seen = [], set()
     for r in records:
         key = (r["M"], r["N"], r["K"])
-        if r["vec"] or key in seen:
+        if key in seen:
             continue
         seen.add(key)
         rows.append(r)
     if not rows:
-        raise ValueError("no scalar-variant records with rates")
+        raise ValueError("no records with rates")
     common = set(rows[0]["rates"])
     for r in rows[1:]:
         common &= set(r["rates"])
     cols = sorted(common, key=lambda t: tuple(int(x) for x in t.split(",")))
     lines = [
-        "// scalar_rates.inc -- measured-rate table for scalar-variant shapes.",
+        "// measured_rates.inc -- measured-rate table for shapes off the rules.",
         "//",
         f"// Written by `{command}`",
         "// from off-table dispatch studies (tune.py --off-table): each row is a",
-        "// seeded shape that runs the scalar variant, with every column tile's",
-        "// rate there as a percentage of the row's fastest column (at least 1).",
-        "// select_config in sgemm_api.hip describes how the dispatch reads it.",
+        "// seeded shape, with every column tile's rate there as a percentage of",
+        "// the row's fastest column (at least 1); kScalarRows hold shapes that run",
+        "// the scalar variant, kVectorRows shapes that run the float4 variant.",
+        "// select_config in sgemm_api.hip describes how the dispatch reads them.",
         "// Tile order: {BM, BN, BK, WM, WN, WNITER, TM, TN, NT, path, swz, opt}.",
         "",
         "static constexpr Tile kRateTiles[] = {",
     ]
     for i, t in enumerate(cols):
         lines.append("    {%s},  // column %d" % (t.replace(",", ", "), i))
-    lines += ["};", "", "static const RateRow kRateRows[] = {"]
-    for r in sorted(rows, key=lambda r: (r["M"], r["N"], r["K"])):
-        best = max(r["rates"][t] for t in cols)
-        pct = [max(1, int(round(100.0 * r["rates"][t] / best))) for t in cols]
-        lines.append("    {%d, %d, %d, {%s}},  // best %.1f TFLOP/s" % (
-            r["M"], r["N"], r["K"], ", ".join(map(str, pct)), best))
-    lines += ["};", ""]
+    lines.append("};")
+    counts = {}
+    for name, vec in (("kScalarRows", False), ("kVectorRows", True)):
+        sel = sorted((r for r in rows if bool(r["vec"]) == vec), key=lambda r: (r["M"], r["N"], r["K"]))
+        counts[vec] = len(sel)
+        lines += ["", f"static const RateRow {name}[] = {{"]
+        for r in sel:
+            best = max(r["rates"][t] for t in cols)
+            pct = [max(1, int(round(100.0 * r["rates"][t] / best))) for t in cols]
+            lines.append("    {%d, %d, %d, {%s}},  // best %.1f TFLOP/s" % (
+                r["M"], r["N"], r["K"], ", ".join(map(str, pct)), best))
+        if not sel:
+            lines.append("    {0, 0, 0, {}},  // none measured")
+        lines.append("};")
+    lines.append("")
     with open(path, "w") as f:
         f.write("\n".join(lines))
-    return cols, len(rows)
+    return cols, counts[False], counts[True]
 
 
 def update_table(path, results, lead=0.01):
@@ -412,7 +445,7 @@ def write_table(best_by_shape, path, defaults):
         "//",
         "// kTuned lists shapes with the tuple the autotuner measured fastest on",
         "// them (fp32_gemm_amd/tune.py); other shapes choose among the rules, or",
-        "// from the measured-rate table of scalar_rates.inc, as select_config in",
+        "// from the measured-rate table of measured_rates.inc, as select_config in",
         "// sgemm_api.hip describes.  Tuple order:",
         "// {BM, BN, BK, WM, WN, WNITER, TM, TN, NT, path, swz, opt}.",
         "",
@@ -466,6 +499,13 @@ def main():
     ap.add_argument("--off-table", type=int, default=None, metavar="SEED",
                     help="dispatch study on seeded shapes off the table (writes --out and "
                          "--summary-out), no sweep")
+    ap.add_argument("--shapes", default=None,
+                    help="with --off-table: time these shapes (MxNxK, comma-separated) instead "
+                         "of seeded ones")
+    ap.add_argument("--mix", default="standard", choices=("standard", "large"),
+                    help="with --off-table: the distribution of the seeded shapes")
+    ap.add_argument("--aligned", action="store_true",
+                    help="with --off-table: round N and K up to multiples of 4 (float4 variant)")
     ap.add_argument("--rate-table", default=None, metavar="FILES",
                     help="write --rate-table-out from these off-table records (comma-separated "
                          "JSONL files of --off-table runs); no GPU needed")
@@ -476,10 +516,11 @@ def main():
         # The command as written into the table names the record files
         # without their directory.
         names = ",".join(os.path.basename(f) for f in args.rate_table.split(","))
-        cols, n = write_rate_table(recs, args.rate_table_out,
-                                   f"python -m fp32_gemm_amd.tune --rate-table {names} "
-                                   f"--rate-table-out {args.rate_table_out}")
-        print(f"[rate-table] {n} rows x {len(cols)} columns -> {args.rate_table_out}")
+        cols, ns, nv = write_rate_table(recs, args.rate_table_out,
+                                        f"python -m fp32_gemm_amd.tune --rate-table {names} "
+                                        f"--rate-table-out {args.rate_table_out}")
+        print(f"[rate-table] {ns} scalar and {nv} float4 rows x {len(cols)} columns -> "
+              f"{args.rate_table_out}")
         return 0
     if args.best:
         recs = [json.loads(l) for l in open(args.out)]
@@ -492,7 +533,9 @@ def main():
         raise SystemExit("tune: current device is not gfx950")
     if args.off_table is not None:
         off_table(args.off_table, dev, args.out, args.summary_out,
-                  "python -m fp32_gemm_amd.tune " + " ".join(sys.argv[1:]))
+                  "python -m fp32_gemm_amd.tune " + " ".join(sys.argv[1:]), aligned=args.aligned,
+                  shapes=[tuple(int(x) for x in sh.split("x")) for sh in args.shapes.split(",")]
+                  if args.shapes else None, mix=args.mix)
         return 0
     if args.retime:
         shapes = {**inputs.WORKLOADS, **inputs.TUNING_EXTRA}

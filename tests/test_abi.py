@@ -129,35 +129,33 @@ def test_tuned_table_tuples_are_compiled():
 
 
 def test_off_table_rules_follow_the_variant():
-    # Off the table, a shape takes a rule tuned on a shape of its own variant:
-    # the ragged rules (tuned where only the 4-byte scalar variant runs) serve
+    # Outside the measured-rate table's range (M or N below 128, or K below
+    # 32) a shape takes a rule tuned on a shape of its own variant: the
+    # ragged rules (tuned where only the 4-byte scalar variant runs) serve
     # unaligned shapes, the aligned rules aligned ones, even where a ragged
     # rule's shape is nearer.  Without a device the fill check (it needs the
     # device's occupancy) counts every launch as full, and the nearest such
-    # rule is reported.  (Unaligned shapes inside the measured-rate table's
-    # range choose from that table instead: the next test.)
+    # rule is reported.
     rules = _table_rules()
     import torch
     if torch.cuda.is_available():
         pytest.skip("the fill check changes the choice on a device")
 
-    def nearest(M, N, K, aligned):
+    def nearest(M, N, K, aligned=None):
         d = {s: sum(math.log2(a / b) ** 2 for a, b in zip((M, N, K), s))
-             for s in rules if (s[2] % 4 == 0 and s[1] % 4 == 0) == aligned}
-        return rules[min(d, key=d.get)]
+             for s in rules if aligned is None or (s[2] % 4 == 0 and s[1] % 4 == 0) == aligned}
+        return min(d, key=d.get)
 
-    # 12288 x 12288 x 1024 lies a hair nearer 4097 x 4095 x 4093 than 4096^3.
-    d = {s: sum(math.log2(a / b) ** 2 for a, b in zip((12288, 12288, 1024), s))
-         for s in [(4096, 4096, 4096), (4097, 4095, 4093)]}
-    assert d[(4097, 4095, 4093)] < d[(4096, 4096, 4096)]
-    code, p = plan(12288, 12288, 1024, 1024, 12288, 12288)
+    # 120 x 1500 x 776 lies nearest the ragged 1000 x 1500 x 777 rule.
+    assert nearest(120, 1500, 776) == (1000, 1500, 777)
+    code, p = plan(120, 1500, 776, 776, 1500, 1500)
     assert code == 0 and p["vector_variant"] == 1
-    assert tuple(fg.config_info(p["cfg_id"])["tuple"]) == nearest(12288, 12288, 1024, True)
-    assert tuple(fg.config_info(p["cfg_id"])["tuple"]) != rules[(4097, 4095, 4093)]
+    assert tuple(fg.config_info(p["cfg_id"])["tuple"]) == rules[nearest(120, 1500, 776, True)]
+    assert nearest(120, 1500, 776, True) != (1000, 1500, 777)
     for M, N, K in ((100, 3001, 2999), (5000, 64, 777), (3000, 3001, 20)):
         code, p = plan(M, N, K, K, N, N)
         assert code == 0 and p["vector_variant"] == 0
-        assert tuple(fg.config_info(p["cfg_id"])["tuple"]) == nearest(M, N, K, False), (M, N, K)
+        assert tuple(fg.config_info(p["cfg_id"])["tuple"]) == rules[nearest(M, N, K, False)], (M, N, K)
 
 
 def _table_rules():
@@ -167,39 +165,45 @@ def _table_rules():
 
 
 def _rate_table():
-    text = open(os.path.join(ROOT, "fp32_gemm_amd", "csrc", "scalar_rates.inc")).read()
-    tiles_text = text[text.index("kRateTiles[]"):text.index("kRateRows[]")]
+    text = open(os.path.join(ROOT, "fp32_gemm_amd", "csrc", "measured_rates.inc")).read()
+    tiles_text = text[text.index("kRateTiles[]"):text.index("kScalarRows[]")]
     cols = [tuple(int(x) for x in t.split(",")) for t in re.findall(r"\{([\d, ]+)\},\s*// column", tiles_text)]
-    rows = [((int(M), int(N), int(K)), [int(x) for x in pct.split(",")])
-            for M, N, K, pct in re.findall(r"\{(\d+), (\d+), (\d+), \{([\d, ]+)\}\}",
-                                           text[text.index("kRateRows[]"):])]
-    return cols, rows
+
+    def rows(body):
+        return [((int(M), int(N), int(K)), [int(x) for x in pct.split(",")])
+                for M, N, K, pct in re.findall(r"\{(\d+), (\d+), (\d+), \{([\d, ]+)\}\}", body)]
+
+    scalar = rows(text[text.index("kScalarRows[]"):text.index("kVectorRows[]")])
+    vector = rows(text[text.index("kVectorRows[]"):])
+    return cols, scalar, vector
 
 
 def test_rate_table_is_well_formed():
-    # Every column names a compiled tuple; every row is a distinct shape that
-    # runs the scalar variant, holds one percentage per column, and has its
-    # fastest column at 100.
-    cols, rows = _rate_table()
+    # Every column names a compiled tuple; every row is a distinct shape of
+    # its variant (N or K not a multiple of 4 for the scalar rows, both
+    # multiples of 4 for the float4 rows), holds one percentage per column,
+    # and has its fastest column at 100.
+    cols, scalar, vector = _rate_table()
     compiled = {tuple(c["tuple"]) for c in fg.configs()}
-    assert cols and rows and len(cols) <= 32
+    assert cols and scalar and vector and len(cols) <= 32
     assert all(c in compiled for c in cols)
-    assert len({s for s, _ in rows}) == len(rows)
-    for (M, N, K), pct in rows:
-        assert not (N % 4 == 0 and K % 4 == 0), (M, N, K)
-        assert len(pct) == len(cols) and max(pct) == 100 and min(pct) >= 1
+    for rows, aligned in ((scalar, False), (vector, True)):
+        assert len({s for s, _ in rows}) == len(rows)
+        for (M, N, K), pct in rows:
+            assert (N % 4 == 0 and K % 4 == 0) == aligned, (M, N, K)
+            assert len(pct) == len(cols) and max(pct) == 100 and min(pct) >= 1
 
 
-def test_scalar_shapes_follow_the_rate_table():
-    # An unaligned shape without an exact rule, with M, N >= 128 and K >= 32,
-    # takes the column with the highest sum over the 16 nearest rows (in
+def test_off_rule_shapes_follow_the_rate_table():
+    # A shape without an exact rule, with M, N >= 128 and K >= 32, takes the
+    # column with the highest sum over the 16 nearest rows of its variant (in
     # log2 M, log2 N and log2 K, the K difference weighing one half) of
     # exp(-squared distance) * log(percentage / 100).  The choice needs no
     # device, so this holds on any host.
-    cols, rows = _rate_table()
+    cols, scalar, vector = _rate_table()
     rules = _table_rules()
 
-    def expected(M, N, K):
+    def expected(M, N, K, rows):
         x = (math.log2(M), math.log2(N), math.log2(K))
         d = sorted(((x[0] - math.log2(s[0])) ** 2 + (x[1] - math.log2(s[1])) ** 2 +
                     0.5 * (x[2] - math.log2(s[2])) ** 2, i) for i, (s, _) in enumerate(rows))[:16]
@@ -207,19 +211,24 @@ def test_scalar_shapes_follow_the_rate_table():
                  for c in range(len(cols))]
         return cols[max(range(len(cols)), key=lambda c: score[c])]
 
-    shapes = [(4000, 4001, 4003), (3603, 2045, 218), (1269, 7747, 321), (706, 1029, 963),
-              (128, 129, 32), (20001, 300, 5001), (1000, 1000, 1001)]
-    shapes += [s for s, _ in rows[:3]]   # a row's own shape
-    for M, N, K in shapes:
+    cases = [((4000, 4001, 4003), scalar), ((3603, 2045, 218), scalar), ((1269, 7747, 321), scalar),
+             ((706, 1029, 963), scalar), ((128, 129, 32), scalar), ((20001, 300, 5001), scalar),
+             ((1000, 1000, 1001), scalar), ((4000, 4000, 4000), vector), ((12288, 12288, 1024), vector),
+             ((128, 128, 32), vector), ((894, 324, 5236), vector), ((30000, 20000, 8192), vector)]
+    cases += [(s, scalar) for s, _ in scalar[:2]] + [(s, vector) for s, _ in vector[:2]]
+    for (M, N, K), rows in cases:
         assert (M, N, K) not in rules
         code, p = plan(M, N, K, K, N, N)
-        assert code == 0 and p["vector_variant"] == 0
-        assert tuple(fg.config_info(p["cfg_id"])["tuple"]) == expected(M, N, K), (M, N, K)
+        assert code == 0 and p["vector_variant"] == (rows is vector)
+        assert tuple(fg.config_info(p["cfg_id"])["tuple"]) == expected(M, N, K, rows), (M, N, K)
+    # Unaligned operands of an aligned shape read the scalar rows.
+    code, p = plan(4000, 4000, 4000, 4001, 4000, 4000)
+    assert code == 0 and p["vector_variant"] == 0
+    assert tuple(fg.config_info(p["cfg_id"])["tuple"]) == expected(4000, 4000, 4000, scalar)
     # An exact rule still wins over the table.
     for s, t in rules.items():
-        if not (s[1] % 4 == 0 and s[2] % 4 == 0):
-            code, p = plan(*s, s[2], s[1], s[1])
-            assert tuple(fg.config_info(p["cfg_id"])["tuple"]) == t
+        code, p = plan(*s, s[2], s[1], s[1])
+        assert tuple(fg.config_info(p["cfg_id"])["tuple"]) == t
 
 
 def test_quick_return_and_no_device():

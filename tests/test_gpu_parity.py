@@ -679,7 +679,8 @@ def test_overlap_rejected(fg, dev):
 
 def _launch_efficiency(c, M, N, K, slots):
     """Busy share of the resident slots, as the launcher splits a partly
-    filled last wave of a split-K configuration."""
+    filled last wave of a split-K configuration; 0 for a launch that splits
+    every tile."""
     tiles = -(-M // c["BM"]) * -(-N // c["BN"])
     grid = tiles
     if c["opt"] & 8:
@@ -687,26 +688,46 @@ def _launch_efficiency(c, M, N, K, slots):
         if tail and 2 * tail <= slots and nk >= 2:
             s = min(slots // tail, nk)
             if s >= 2:
+                if tail == tiles:
+                    return 0.0
                 grid = tiles - tail + tail * s
     return grid / (-(-grid // slots) * slots)
 
 
-def test_off_table_dispatch_fills_the_device(fg, dev):
-    # Shapes outside the tuned table: the chosen configuration keeps at least
-    # 85 % of the resident slots busy (its split of a partly filled last wave
-    # counted), and where a 256 x 256 rule can do that it is the one chosen.
+def test_rule_dispatch_fills_the_device(fg, dev):
+    # Aligned shapes outside the measured-rate table's range (M or N below
+    # 128) with at least 2^30 FLOP and K >= 256 choose among the aligned
+    # rules: of those whose launch keeps at least 85 % of the resident slots
+    # busy (the split of a partly filled last wave counted, a launch that
+    # splits every tile not), one with the largest block tile; with none,
+    # the nearest rule in (log M, log N, log K).
+    import math
+    import re
+    text = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                             "fp32_gemm_amd", "csrc", "tuned_table.inc")).read()
+    rules = {(int(M), int(N), int(K)): tuple(int(x) for x in t.split(","))
+             for M, N, K, t in re.findall(r"\{(\d+), (\d+), (\d+), \{([\d, ]+)\}\}", text)
+             if int(N) % 4 == 0 and int(K) % 4 == 0}
+    ids = {tuple(c["tuple"]): c["id"] for c in fg.configs()}
     fake = 1 << 40
-    for M, N, K, big in [(6000, 6000, 6000, True), (6144, 6144, 6144, True),
-                         (10000, 10000, 4096, True), (12288, 12288, 1024, True),
-                         (7000, 5000, 3000, True), (5000, 3000, 2000, True),
-                         (3000, 3000, 3000, False), (3500, 3500, 3500, False)]:
+    for M, N, K in [(100, 8192, 8192), (120, 16384, 4096), (8192, 100, 8192), (64, 30000, 4096)]:
+        assert (M, N, K) not in rules and 2 * M * N * K >= 1 << 30
         p = fg.plan(M, N, K, fake, K, 2 * fake, N, 4 * fake, N)
         c = fg.config_info(p["cfg_id"])
-        assert p["slots"] > 0
-        eff = _launch_efficiency(c, M, N, K, p["slots"])
-        log(f"[off-table] {M}x{N}x{K}: {c['tuple']} efficiency {eff:.3f}")
-        assert eff >= 0.85, (M, N, K, c["tuple"], p["slots"])
-        assert (c["BM"] * c["BN"] == 256 * 256) == big, (M, N, K, c["tuple"])
+        eff = {}
+        for t in set(rules.values()):
+            ci = fg.config_info(ids[t])
+            slots = fg.plan(M, N, K, fake, K, 2 * fake, N, 4 * fake, N, ids[t])["slots"]
+            assert slots > 0
+            eff[t] = _launch_efficiency(ci, M, N, K, slots)
+        fit = [t for t, e in eff.items() if e >= 0.85]
+        log(f"[rule fill] {M}x{N}x{K}: {c['tuple']}, {len(fit)} rules fill the device")
+        if fit:
+            assert eff[tuple(c["tuple"])] >= 0.85, (M, N, K, c["tuple"])
+            assert c["BM"] * c["BN"] == max(t[0] * t[1] for t in fit), (M, N, K, c["tuple"])
+        else:
+            d = {s: sum(math.log2(a / b) ** 2 for a, b in zip((M, N, K), s)) for s in rules}
+            assert tuple(c["tuple"]) == rules[min(d, key=d.get)], (M, N, K, c["tuple"])
 
 
 def test_graph_capture_replays(fg, dev, orc):

@@ -47,22 +47,26 @@ def test_update_moves_only_rules_with_a_clear_lead(tmp_path):
 
 
 def test_rate_table_rows_and_columns(tmp_path):
-    # Scalar-variant records only, each shape once (the first record), the
-    # columns the tuples timed on every row, percentages of the row's best
-    # rounded and floored at 1.
+    # Rows per variant, each shape once (the first record), the columns the
+    # tuples timed on every row, percentages of the row's best rounded and
+    # floored at 1; a variant without records gets an empty marker row.
     a, b, c = "64,64,16,32,32,1,16,1,256,1,32,18", "128,128,16,64,64,4,4,1,256,2,64,24", \
         "256,256,32,128,64,2,16,1,512,1,32,27"
     recs = [
         dict(M=1000, N=1001, K=999, vec=False, rates={a: 50.0, b: 100.0, c: 0.4}),
         dict(M=300, N=301, K=302, vec=False, rates={a: 80.0, b: 40.0}),
         dict(M=1000, N=1001, K=999, vec=False, rates={a: 100.0, b: 10.0}),   # repeat: ignored
-        dict(M=512, N=512, K=512, vec=True, rates={a: 1.0, b: 2.0}),         # float4: ignored
+        dict(M=512, N=512, K=512, vec=True, rates={a: 1.0, b: 2.0, c: 3.0}),
     ]
     path = tmp_path / "rates.inc"
-    cols, n = tune.write_rate_table(recs, str(path), "cmd")
-    assert cols == [a, b] and n == 2
+    cols, ns, nv = tune.write_rate_table(recs, str(path), "cmd")
+    assert cols == [a, b] and ns == 2 and nv == 1
     text = path.read_text()
     assert "{64, 64, 16, 32, 32, 1, 16, 1, 256, 1, 32, 18},  // column 0" in text
-    assert "{300, 301, 302, {100, 50}}" in text and "{1000, 1001, 999, {50, 100}}" in text
-    assert text.index("{300, 301, 302") < text.index("{1000, 1001, 999")
-    assert "512, 512, 512" not in text and "`cmd`" in text
+    scalar = text[text.index("kScalarRows[]"):text.index("kVectorRows[]")]
+    vector = text[text.index("kVectorRows[]"):]
+    assert "{300, 301, 302, {100, 50}}" in scalar and "{1000, 1001, 999, {50, 100}}" in scalar
+    assert scalar.index("{300, 301, 302") < scalar.index("{1000, 1001, 999")
+    assert "{512, 512, 512, {50, 100}}" in vector and "`cmd`" in text
+    cols, ns, nv = tune.write_rate_table(recs[:2], str(path), "cmd")
+    assert nv == 0 and "{0, 0, 0, {}},  // none measured" in path.read_text()
