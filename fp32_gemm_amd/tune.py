@@ -238,7 +238,11 @@ def off_table(seed, dev, out_path, summary_path, command, count=36, aligned=Fals
     [64, 1024] (shapes above 8192^3's work skipped).  The large mix, all
     log-uniform: a third each with M, N, K in [4096, 16384], M, N in
     [4096, 16384] with K in [16, 512], and M, N in [2048, 16384] with K in
-    [8192, 65536] (shapes above 16384^3's work skipped).  With `aligned`, N
+    [8192, 65536] (shapes above 16384^3's work skipped).  The grid mix: M and
+    N drawn from 512, 1024, 1536, 2048, 3072, 4096, 6144, 8192, 12288 and
+    16384, K from 64, 128, 256, 384, 512, 768, 1024, 1536, 2048, 3072, 4096,
+    6144, 8192, 12288 and 16384 (above 16384^3's work skipped; each shape
+    once).  With `aligned`, N
     and K are rounded up to multiples of 4, so every shape runs the float4
     variant.  Per shape the tuned dispatch's choice, the tuple of every
     table rule and torch.mm are timed interleaved (3 warm-up launches each,
@@ -259,10 +263,19 @@ def off_table(seed, dev, out_path, summary_path, command, count=36, aligned=Fals
     def log_uniform(lo, hi):
         return int(round(np.exp(rng.uniform(np.log(lo), np.log(hi)))))
 
-    cap = 16384 ** 3 if mix == "large" else 8192 ** 3
+    cap = 16384 ** 3 if mix in ("large", "grid") else 8192 ** 3
+    grid_mn = (512, 1024, 1536, 2048, 3072, 4096, 6144, 8192, 12288, 16384)
+    grid_k = (64, 128, 256, 384, 512, 768, 1024, 1536, 2048, 3072, 4096, 6144, 8192, 12288, 16384)
+    done = set()
     for i in range(len(shapes) if shapes else count):
         if shapes:
             M, N, K = shapes[i]
+        elif mix == "grid":
+            M, N = (int(x) for x in rng.choice(grid_mn, 2))
+            K = int(rng.choice(grid_k))
+            if (M, N, K) in done:
+                continue
+            done.add((M, N, K))
         elif mix == "large":
             if i % 3 == 0:
                 M, N, K = (log_uniform(4096, 16384) for _ in range(3))
@@ -397,6 +410,32 @@ def write_rate_table(records, path, command):
     return cols, counts[False], counts[True]
 
 
+def write_rate_table_gap(swept, path, command):
+    """Markdown table: per swept shape, the fastest of every swept tuple
+    against the fastest tile of the measured-rate table (short protocol)."""
+    table = set()
+    for line in open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc",
+                                  "measured_rates.inc")):
+        if "// column" in line:
+            table.add(tuple(int(x) for x in line.split("{")[1].split("}")[0].split(",")))
+    lines = ["# The measured-rate table's tiles against a sweep of every tuple", "",
+             f"Command: `{command}`", "",
+             "Per shape, every swept tuple was checked exactly and timed with the short protocol "
+             "(3 warm-up, 10 timed launches; A, B ~ N(0,1), beta = 0); the fastest of them against "
+             "the fastest of the measured-rate table's tiles.", "",
+             "| shape | swept | fastest tuple | TFLOP/s | fastest table tile | TFLOP/s | ratio |",
+             "|---|---|---|---|---|---|---|"]
+    for name, rs in swept.items():
+        top = max(rs, key=lambda r: r["tflops"])
+        tab = [r for r in rs if tuple(r["tuple"]) in table]
+        tb = max(tab, key=lambda r: r["tflops"]) if tab else None
+        lines.append(f"| {name} | {len(rs)} | {','.join(map(str, top['tuple']))} | {top['tflops']:.1f} | "
+                     + (f"{','.join(map(str, tb['tuple']))} | {tb['tflops']:.1f} | "
+                        f"{tb['tflops'] / top['tflops']:.3f} |" if tb else "- | - | - |"))
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def update_table(path, results, lead=0.01):
     """Rewrites the rules of the re-timed shapes in an existing table: a rule
     moves to the fastest re-timed tuple only where that tuple leads the
@@ -500,9 +539,11 @@ def main():
                     help="dispatch study on seeded shapes off the table (writes --out and "
                          "--summary-out), no sweep")
     ap.add_argument("--shapes", default=None,
-                    help="with --off-table: time these shapes (MxNxK, comma-separated) instead "
-                         "of seeded ones")
-    ap.add_argument("--mix", default="standard", choices=("standard", "large"),
+                    help="shapes MxNxK, comma-separated: with --off-table, time these instead of "
+                         "seeded ones; otherwise sweep them (instead of --workloads) and write to "
+                         "--summary-out the fastest tuple against the fastest measured-rate table "
+                         "tile")
+    ap.add_argument("--mix", default="standard", choices=("standard", "large", "grid"),
                     help="with --off-table: the distribution of the seeded shapes")
     ap.add_argument("--aligned", action="store_true",
                     help="with --off-table: round N and K up to multiples of 4 (float4 variant)")
@@ -567,9 +608,15 @@ def main():
         if rec.get("protocol") == "long" or not rec["exact"]:
             print(json.dumps(rec), flush=True)
 
-    bests, per_path = [], {}
+    bests, per_path, swept = [], {}, {}
     ranked = None  # the --prune-from shape's configurations, fastest first per path
     shapes = {**inputs.WORKLOADS, **inputs.TUNING_EXTRA}
+    if args.shapes:
+        # Ad-hoc shapes: A, B ~ N(0, 1), C ~ U[-1, 1], alpha 1, beta 0.
+        adhoc = [tuple(int(x) for x in sh.split("x")) for sh in args.shapes.split(",")]
+        shapes = {f"{M}x{N}x{K}": inputs.Workload(f"{M}x{N}x{K}", M, N, K, "normal", "uniform", 1.0,
+                                                  0.0, 7) for M, N, K in adhoc}
+        args.workloads = ",".join(shapes)
     names = sorted(args.workloads.split(","), key=lambda n: (n != args.prune_from, model.flops(
         shapes[n].M, shapes[n].N, shapes[n].K)))
     progress = lambda msg: print(msg, flush=True)
@@ -600,7 +647,11 @@ def main():
         print(f"[tune] {name}: best cfg {best['cfg_id']} {best['tuple']} {best['ms']:.4f} ms "
               f"{best['tflops']:.1f} TFLOP/s ({time.time() - t0:.0f} s)", flush=True)
         bests.append(best)
-    if args.summary_out:
+        swept[name] = [r for r in results if r.get("protocol") == "short" and r["exact"]]
+    if args.shapes and args.summary_out:
+        write_rate_table_gap(swept, args.summary_out, "python -m fp32_gemm_amd.tune " +
+                             " ".join(sys.argv[1:]))
+    elif args.summary_out:
         write_summary(per_path, args.summary_out, "python -m fp32_gemm_amd.tune " +
                       " ".join(sys.argv[1:]), args.finalists)
     if args.table_out:

@@ -198,8 +198,9 @@ def test_off_rule_shapes_follow_the_rate_table():
     # A shape without an exact rule, with M, N >= 128 and K >= 32, takes the
     # column with the highest sum over the 16 nearest rows of its variant (in
     # log2 M, log2 N and log2 K, the K difference weighing one half) of
-    # exp(-squared distance) * log(percentage / 100).  The choice needs no
-    # device, so this holds on any host.
+    # exp(-squared distance) * log(percentage / 100); a shape that is a row
+    # takes that row's fastest column.  The choice needs no device, so this
+    # holds on any host.
     cols, scalar, vector = _rate_table()
     rules = _table_rules()
 
@@ -207,6 +208,9 @@ def test_off_rule_shapes_follow_the_rate_table():
         x = (math.log2(M), math.log2(N), math.log2(K))
         d = sorted(((x[0] - math.log2(s[0])) ** 2 + (x[1] - math.log2(s[1])) ** 2 +
                     0.5 * (x[2] - math.log2(s[2])) ** 2, i) for i, (s, _) in enumerate(rows))[:16]
+        if d[0][0] == 0.0:
+            pct = rows[d[0][1]][1]
+            return cols[pct.index(max(pct))]
         score = [sum(math.exp(-dd) * math.log(rows[i][1][c] / 100.0) for dd, i in d)
                  for c in range(len(cols))]
         return cols[max(range(len(cols)), key=lambda c: score[c])]

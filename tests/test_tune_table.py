@@ -70,3 +70,17 @@ def test_rate_table_rows_and_columns(tmp_path):
     assert "{512, 512, 512, {50, 100}}" in vector and "`cmd`" in text
     cols, ns, nv = tune.write_rate_table(recs[:2], str(path), "cmd")
     assert nv == 0 and "{0, 0, 0, {}},  // none measured" in path.read_text()
+
+
+def test_rate_table_gap_summary(tmp_path):
+    # The sweep summary for ad-hoc shapes names the fastest swept tuple and
+    # the fastest tile that the measured-rate table lists.
+    text = open("fp32_gemm_amd/csrc/measured_rates.inc").read()
+    first = text[text.index("kRateTiles[]"):].split("{", 2)[2].split("}")[0]
+    in_table = [int(x) for x in first.split(",")]
+    other = [1, 2, 3]
+    swept = {"100x200x300": [dict(tuple=other, tflops=50.0), dict(tuple=in_table, tflops=40.0)]}
+    path = tmp_path / "gap.md"
+    tune.write_rate_table_gap(swept, str(path), "cmd")
+    row = [l for l in path.read_text().split("\n") if l.startswith("| 100x200x300")][0]
+    assert "| 1,2,3 | 50.0 |" in row and f"| {','.join(map(str, in_table))} | 40.0 | 0.800 |" in row
