@@ -242,7 +242,9 @@ def off_table(seed, dev, out_path, summary_path, command, count=36, aligned=Fals
     N drawn from 512, 1024, 1536, 2048, 3072, 4096, 6144, 8192, 12288 and
     16384, K from 64, 128, 256, 384, 512, 768, 1024, 1536, 2048, 3072, 4096,
     6144, 8192, 12288 and 16384 (above 16384^3's work skipped; each shape
-    once).  With `aligned`, N
+    once).  The short-K grid, not drawn but enumerated (seed and count
+    unused): every M, N in 4096, 6144, 8192, 12288, 16384 with K in 128,
+    192, 256, 384, 512, 768.  With `aligned`, N
     and K are rounded up to multiples of 4, so every shape runs the float4
     variant.  Per shape the tuned dispatch's choice, the tuple of every
     table rule and torch.mm are timed interleaved (3 warm-up launches each,
@@ -267,6 +269,9 @@ def off_table(seed, dev, out_path, summary_path, command, count=36, aligned=Fals
     grid_mn = (512, 1024, 1536, 2048, 3072, 4096, 6144, 8192, 12288, 16384)
     grid_k = (64, 128, 256, 384, 512, 768, 1024, 1536, 2048, 3072, 4096, 6144, 8192, 12288, 16384)
     done = set()
+    if mix == "grid-short-k":
+        shapes = [(M, N, K) for M in (4096, 6144, 8192, 12288, 16384)
+                  for N in (4096, 6144, 8192, 12288, 16384) for K in (128, 192, 256, 384, 512, 768)]
     for i in range(len(shapes) if shapes else count):
         if shapes:
             M, N, K = shapes[i]
@@ -339,7 +344,8 @@ def off_table(seed, dev, out_path, summary_path, command, count=36, aligned=Fals
         of_best = [r["chosen_tflops"] / r["best_tflops"] for r in recs]
         vs_torch = [r["chosen_tflops"] / r["torch_tflops"] for r in recs]
         kind = "aligned " if aligned else ""
-        title = "given shapes" if shapes else f"seeded {kind}off-table shapes ({mix} mix, seed {seed})"
+        title = (f"the {mix} shapes" if mix == "grid-short-k" else "given shapes" if shapes
+                 else f"seeded {kind}off-table shapes ({mix} mix, seed {seed})")
         lines = [f"# Dispatch on {title}", "", f"Command: `{command}`", "",
                  off_table.__doc__.split("\n\n")[0].replace("\n    ", " ").strip(), "",
                  f"{len(recs)} shapes ({sum(not r['vec'] for r in recs)} scalar-variant). The dispatch's "
@@ -543,7 +549,7 @@ def main():
                          "seeded ones; otherwise sweep them (instead of --workloads) and write to "
                          "--summary-out the fastest tuple against the fastest measured-rate table "
                          "tile")
-    ap.add_argument("--mix", default="standard", choices=("standard", "large", "grid"),
+    ap.add_argument("--mix", default="standard", choices=("standard", "large", "grid", "grid-short-k"),
                     help="with --off-table: the distribution of the seeded shapes")
     ap.add_argument("--aligned", action="store_true",
                     help="with --off-table: round N and K up to multiples of 4 (float4 variant)")
