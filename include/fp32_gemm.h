@@ -147,19 +147,25 @@ typedef struct sgemm_plan_t {
 
 /* Validates like sgemm_ex (same status codes, no device check) and fills
  * *out.  cfg_id < 0 selects the tuned configuration: the exact-shape rule;
- * else, among the rules tuned on shapes that run the same variant (float4 or
- * scalar; all rules if none does), from 2^30 FLOP up and with K >= 256 the
- * largest block tile whose launch keeps at least 85 % of the resident
- * workgroup slots busy (a
+ * else, with M, N >= 128 and K >= 32, the tile chosen from the library's
+ * table of measured rates (seeded shapes of the same variant, float4 or
+ * scalar, on which every table tile was timed): a measured shape's fastest
+ * tile, otherwise the tile with the highest sum over the 16 nearest measured
+ * shapes in (log2 M, log2 N, log2 K), the K difference weighing 1/2, of
+ * exp(-squared distance) * log(rate / that shape's best rate).  Other shapes
+ * choose among the rules tuned on shapes of the same variant (all rules if
+ * none is): from 2^30 FLOP up and with K >= 256 the largest block tile whose
+ * launch keeps at least 85 % of the resident workgroup slots busy (a
  * split-K tuple's split of a partly filled last wave counted; a launch that
- * would split every tile does not count as filling), ties going to
- * the busier launch and then to the nearer rule in (log M, log N, log K);
- * for smaller or shorter-K products, or when no rule fills the device, the
+ * would split every tile does not count as filling), ties going to the
+ * busier launch and then to the nearer rule in (log M, log N, log K); for
+ * smaller or shorter-K products, or when no rule fills the device, the
  * nearest rule.
  * Split-K tiles add partial sums with atomics, so their last bits may differ
  * from run to run (within the accuracy bound).  The split decision and the
  * fill check need the device's compute units and occupancy; without a device
- * the nearest rule and no split are reported. */
+ * the fill check is skipped (the nearest rule) and no split is reported; the
+ * rate table needs no device. */
 int sgemm_plan(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
                int64_t ldb, const float* C, int64_t ldc, int32_t cfg_id, sgemm_plan_t* out);
 
