@@ -96,6 +96,14 @@ enum Opt : int {
 
 constexpr int stages_of(const Tile& t) { return 2 + ((t.opt & kOptStagesMask) >> kOptStagesShift); }
 
+// Tuples whose scalar variant keeps 16-byte loads for A (after the first K
+// slice) and for B when N % 4 == 0: direct-LDS matrix-core tiles below
+// 256 x 256 (the kernels' hybrid scalar body; with 4-byte B loads the
+// registers of the larger tiles overflow).
+constexpr bool hybrid_scalar_tile(const Tile& t) {
+  return (t.opt & kOptDirectLds) != 0 && t.path != kPathValu && t.BM * t.BN < 256 * 256;
+}
+
 // Wave groups a k-sliced tuple splits its K loop over (1 otherwise), and the
 // tuple one group runs: the same tile at NT / 2 threads without the option.
 constexpr int kslices_of(const Tile& t) { return (t.opt & kOptKSlice) ? 2 : 1; }

@@ -231,7 +231,7 @@ _RULE = re.compile(r"^(\s*)\{(\d+), (\d+), (\d+), \{([-\d, ]+)\}\},\s*// ([^:]*)
 
 
 def off_table(seed, dev, out_path, summary_path, command, count=36, aligned=False, shapes=None,
-              mix="standard"):
+              mix="standard", n4=False):
     """Dispatch study on seeded shapes that no rule was tuned on.  The
     standard mix: a third each with M, N, K uniform in [512, 8192],
     log-uniform in [256, 16384], and M, N in [1024, 8192] with K in
@@ -246,7 +246,8 @@ def off_table(seed, dev, out_path, summary_path, command, count=36, aligned=Fals
     unused): every M, N in 4096, 6144, 8192, 12288, 16384 with K in 128,
     192, 256, 384, 512, 768.  With `aligned`, N
     and K are rounded up to multiples of 4, so every shape runs the float4
-    variant.  Per shape the tuned dispatch's choice, the tuple of every
+    variant; with `n4`, N is rounded up to a multiple of 4 and K moved to the
+    next number when it is one (the scalar variant with 16-byte B loads).  Per shape the tuned dispatch's choice, the tuple of every
     table rule and torch.mm are timed interleaved (3 warm-up launches each,
     then 6 rounds of one 3-launch batch of each in turn; A, B normal, beta
     = 0); the summary reports the dispatch's rate against the best rule's
@@ -297,6 +298,8 @@ def off_table(seed, dev, out_path, summary_path, command, count=36, aligned=Fals
             K = int(rng.integers(64, 1025))
         if aligned:
             N, K = -(-N // 4) * 4, -(-K // 4) * 4
+        if n4:
+            N, K = -(-N // 4) * 4, K + 1 if K % 4 == 0 else K
         if not shapes and M * N * K > cap:
             continue
         A = torch.randn(M, K, device=dev)
@@ -343,7 +346,7 @@ def off_table(seed, dev, out_path, summary_path, command, count=36, aligned=Fals
         g = lambda xs: float(np.exp(np.mean(np.log(xs))))
         of_best = [r["chosen_tflops"] / r["best_tflops"] for r in recs]
         vs_torch = [r["chosen_tflops"] / r["torch_tflops"] for r in recs]
-        kind = "aligned " if aligned else ""
+        kind = "aligned " if aligned else "N % 4 == 0 scalar-variant " if n4 else ""
         title = (f"the {mix} shapes" if mix == "grid-short-k" else "given shapes" if shapes
                  else f"seeded {kind}off-table shapes ({mix} mix, seed {seed})")
         lines = [f"# Dispatch on {title}", "", f"Command: `{command}`", "",
@@ -551,6 +554,8 @@ def main():
                          "tile")
     ap.add_argument("--mix", default="standard", choices=("standard", "large", "grid", "grid-short-k"),
                     help="with --off-table: the distribution of the seeded shapes")
+    ap.add_argument("--n4", action="store_true",
+                    help="with --off-table: N a multiple of 4, K not (scalar variant, 16-byte B loads)")
     ap.add_argument("--aligned", action="store_true",
                     help="with --off-table: round N and K up to multiples of 4 (float4 variant)")
     ap.add_argument("--rate-table", default=None, metavar="FILES",
@@ -582,7 +587,7 @@ def main():
         off_table(args.off_table, dev, args.out, args.summary_out,
                   "python -m fp32_gemm_amd.tune " + " ".join(sys.argv[1:]), aligned=args.aligned,
                   shapes=[tuple(int(x) for x in sh.split("x")) for sh in args.shapes.split(",")]
-                  if args.shapes else None, mix=args.mix)
+                  if args.shapes else None, mix=args.mix, n4=args.n4)
         return 0
     if args.retime:
         shapes = {**inputs.WORKLOADS, **inputs.TUNING_EXTRA}

@@ -77,7 +77,10 @@ int sgemm(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64_t 
  * stream), with configuration `cfg_id` (0 <= cfg_id < sgemm_num_configs()) or
  * the tuned choice when cfg_id < 0.  Operands that are not 16-byte aligned,
  * whose leading dimensions are not multiples of 4, or with K or N not a
- * multiple of 4 run the scalar-load variant of the same configuration. */
+ * multiple of 4 run the scalar-load variant of the same configuration.  In
+ * that variant the direct-to-LDS matrix-core configurations below 256 x 256
+ * still load A 16 bytes at a time after the first K slice, and B too when
+ * N % 4 == 0. */
 int sgemm_ex(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64_t lda,
              const float* B, int64_t ldb, float beta, float* C, int64_t ldc, void* stream,
              int32_t cfg_id);

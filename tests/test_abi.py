@@ -196,39 +196,51 @@ def test_rate_table_is_well_formed():
 
 def test_off_rule_shapes_follow_the_rate_table():
     # A shape without an exact rule, with M, N >= 128 and K >= 32, takes the
-    # column with the highest sum over the 16 nearest rows of its variant (in
-    # log2 M, log2 N and log2 K, the K difference weighing one half) of
+    # column with the highest sum over the 16 nearest rows (in log2 M, log2 N
+    # and log2 K, the K difference weighing one half) of
     # exp(-squared distance) * log(percentage / 100); a shape that is a row
-    # takes that row's fastest column.  The choice needs no device, so this
-    # holds on any host.
+    # takes that row's fastest column.  Float4 shapes read the float4 rows;
+    # scalar-variant shapes with N % 4 == 0 read them too, among the tiles
+    # whose scalar kernel keeps 16-byte loads (direct-LDS matrix-core tiles
+    # below 256 x 256); other scalar-variant shapes read the scalar rows.
+    # The choice needs no device, so this holds on any host.
     cols, scalar, vector = _rate_table()
     rules = _table_rules()
 
-    def expected(M, N, K, rows):
+    def hybrid(t):
+        return bool(t[11] & 16) and t[9] != 0 and t[0] * t[1] < 256 * 256
+
+    def expected(M, N, K, vec):
+        b16 = not vec and N % 4 == 0
+        rows = vector if vec or b16 else scalar
+        allowed = [c for c in range(len(cols)) if not b16 or hybrid(cols[c])]
         x = (math.log2(M), math.log2(N), math.log2(K))
         d = sorted(((x[0] - math.log2(s[0])) ** 2 + (x[1] - math.log2(s[1])) ** 2 +
                     0.5 * (x[2] - math.log2(s[2])) ** 2, i) for i, (s, _) in enumerate(rows))[:16]
         if d[0][0] == 0.0:
             pct = rows[d[0][1]][1]
-            return cols[pct.index(max(pct))]
-        score = [sum(math.exp(-dd) * math.log(rows[i][1][c] / 100.0) for dd, i in d)
-                 for c in range(len(cols))]
-        return cols[max(range(len(cols)), key=lambda c: score[c])]
+            return cols[max(allowed, key=lambda c: pct[c])]
+        score = {c: sum(math.exp(-dd) * math.log(rows[i][1][c] / 100.0) for dd, i in d) for c in allowed}
+        return cols[max(allowed, key=lambda c: score[c])]
 
-    cases = [((4000, 4001, 4003), scalar), ((3603, 2045, 218), scalar), ((1269, 7747, 321), scalar),
-             ((706, 1029, 963), scalar), ((128, 129, 32), scalar), ((20001, 300, 5001), scalar),
-             ((1000, 1000, 1001), scalar), ((4000, 4000, 4000), vector), ((12288, 12288, 1024), vector),
-             ((128, 128, 32), vector), ((894, 324, 5236), vector), ((30000, 20000, 8192), vector)]
-    cases += [(s, scalar) for s, _ in scalar[:2]] + [(s, vector) for s, _ in vector[:2]]
-    for (M, N, K), rows in cases:
+    cases = [(4000, 4001, 4003), (3603, 2045, 218), (1269, 7747, 321), (706, 1029, 963), (128, 129, 32),
+             (20001, 300, 5001), (1000, 1000, 1001), (4000, 4000, 4000), (12288, 12288, 1024),
+             (128, 128, 32), (894, 324, 5236), (30000, 20000, 8192), (8192, 8192, 8191)]
+    cases += [s for s, _ in scalar[:2]] + [s for s, _ in vector[:2]]
+    kinds = set()
+    for M, N, K in cases:
         assert (M, N, K) not in rules
         code, p = plan(M, N, K, K, N, N)
-        assert code == 0 and p["vector_variant"] == (rows is vector)
-        assert tuple(fg.config_info(p["cfg_id"])["tuple"]) == expected(M, N, K, rows), (M, N, K)
-    # Unaligned operands of an aligned shape read the scalar rows.
+        assert code == 0 and p["vector_variant"] == (N % 4 == 0 and K % 4 == 0)
+        vec = p["vector_variant"] == 1
+        kinds.add("vec" if vec else "b16" if N % 4 == 0 else "scalar")
+        assert tuple(fg.config_info(p["cfg_id"])["tuple"]) == expected(M, N, K, vec), (M, N, K)
+    assert kinds == {"vec", "b16", "scalar"}
+    # Unaligned operands of an aligned shape: the scalar variant, N % 4 == 0.
     code, p = plan(4000, 4000, 4000, 4001, 4000, 4000)
     assert code == 0 and p["vector_variant"] == 0
-    assert tuple(fg.config_info(p["cfg_id"])["tuple"]) == expected(4000, 4000, 4000, scalar)
+    t = tuple(fg.config_info(p["cfg_id"])["tuple"])
+    assert t == expected(4000, 4000, 4000, False) and hybrid(t)
     # An exact rule still wins over the table.
     for s, t in rules.items():
         code, p = plan(*s, s[2], s[1], s[1])

@@ -107,13 +107,14 @@ def _err(got, C64, K, A, B):
 # in M, N and K (several tiles in each direction for every tile size).
 
 SHAPE_VEC = (600, 600, 100)     # K % 4 == N % 4 == 0: float4 variant
-SHAPE_SCALAR = (601, 599, 99)   # scalar variant
+SHAPE_SCALAR = (601, 599, 99)   # scalar variant, N % 4 != 0: 4-byte B loads
+SHAPE_SCALAR_N4 = (601, 600, 99)  # scalar variant, N % 4 == 0: 16-byte B loads
 
 
 @pytest.fixture(scope="module")
 def ragged_cases(orc):
     cases = {}
-    for name, (M, N, K) in (("vec", SHAPE_VEC), ("scalar", SHAPE_SCALAR)):
+    for name, (M, N, K) in (("vec", SHAPE_VEC), ("scalar", SHAPE_SCALAR), ("scalar_n4", SHAPE_SCALAR_N4)):
         A, B, C = inputs.make_random(M, N, K, seed=900 + M)
         r32, r64 = orc.sgemm(A, B, C, 0.5, 3.0)
         Ai, Bi, Ci = inputs.make_small_int(M, N, K, seed=901 + M)
@@ -136,10 +137,10 @@ CHUNKS = 12
 @pytest.mark.parametrize("chunk", range(CHUNKS))
 def test_every_config_both_variants(fg, dev, ragged_cases, chunk):
     cfgs = [c for c in fg.configs() if c["id"] % CHUNKS == chunk]
-    log(f"[parity] chunk {chunk}: {len(cfgs)} configs x 2 variants")
+    log(f"[parity] chunk {chunk}: {len(cfgs)} configs x 3 shapes")
     worst = 0.0
     for c in cfgs:
-        for variant in ("vec", "scalar"):
+        for variant in ("vec", "scalar", "scalar_n4"):
             case = ragged_cases[variant]
             M, N, K = case["shape"]
             log(f"[parity] cfg {c['id']} {c['path_name']} {c['tuple']} {variant} {M}x{N}x{K}")
@@ -155,14 +156,17 @@ def test_every_config_both_variants(fg, dev, ragged_cases, chunk):
     log(f"[parity] worst err {worst:.3e}")
 
 
-@pytest.mark.parametrize("variant", ["vec", "scalar"])
+@pytest.mark.parametrize("variant", ["vec", "scalar", "scalar_n4"])
 def test_every_config_reads_inside_K(fg, dev, orc, variant):
     # A and B sit in NaN-filled buffers: NaN in the lda / ldb padding and in
     # the rows after B's K rows.  A read of any element outside the logical
     # K range would put a NaN into a stored output; the results must instead
     # match the oracle.  (Reads past M or N could only reach outputs that are
-    # never stored; the buffer resources bound those.)
-    M, N, K, pad = (130, 100, 76, 4) if variant == "vec" else (130, 97, 75, 3)
+    # never stored; the buffer resources bound those.)  scalar_n4: K odd and
+    # odd leading dimensions with N % 4 == 0, so the scalar variant's 16-byte
+    # loads run at 4-byte-aligned addresses.
+    M, N, K, pad = {"vec": (130, 100, 76, 4), "scalar": (130, 97, 75, 3),
+                    "scalar_n4": (130, 100, 75, 3)}[variant]
     A, B, C = inputs.make_random(M, N, K, seed=77 + K)
     _, r64 = orc.sgemm(A, B, C, 0.5, 3.0)
     Abig = torch.full((M + 8, K + pad), float("nan"), device=dev)
@@ -220,18 +224,22 @@ def test_split_configs_random_inputs_within_tolerance(fg, dev, orc):
         check_close(cv.result(), r64b, K, A, B, f"split cfg {c['id']} beta=0")
 
 
-@pytest.mark.parametrize("variant", ["vec", "scalar"])
+@pytest.mark.parametrize("variant", ["vec", "scalar", "scalar_n4"])
 def test_direct_lds_configs_short_and_ragged_K(fg, dev, orc, variant):
     # Direct-to-LDS configs run their K slices partial-first: slice 0 holds the
     # K % BK remainder (masked in both operands) and every later slice is
     # whole.  K = 0 (no slice), K below one slice, a one-column tail and a
     # tail one past a whole slice, on ragged M and N, for both load widths;
     # K = 196 / 197 gives BK = 64 tiles an even slice count and BK = 32 an
-    # odd one (the two-slice K loop and its one-slice tail).
+    # odd one (the two-slice K loop and its one-slice tail).  scalar_n4:
+    # N % 4 == 0 with an odd ldc, so the scalar variant runs with 16-byte B
+    # loads, with K % 4 == 0 (a whole-float4 slice 0) and K % 4 != 0.
     cfgs = [c for c in fg.configs() if c["opt"] & 16]
-    N = 92 if variant == "vec" else 91
+    N = 91 if variant == "scalar" else 92
     pad = 4 if variant == "vec" else 5
-    for K in ((0, 4, 36, 64, 196) if variant == "vec" else (0, 1, 33, 65, 197)):
+    Ks = {"vec": (0, 4, 36, 64, 196), "scalar": (0, 1, 33, 65, 197),
+          "scalar_n4": (0, 1, 4, 33, 65, 196, 197)}[variant]
+    for K in Ks:
         log(f"[direct-lds] {variant} 70x{N}x{K}: {len(cfgs)} configs")
         if K == 0:
             C = inputs.make_random(70, N, 1, seed=1700)[2]
@@ -659,6 +667,33 @@ def test_misaligned_pointers_use_scalar_variant(fg, dev, orc):
     fg.sgemm(Aoff, to_dev(B, dev), cv.view, 1.0, 1.0)
     torch.cuda.synchronize()
     check_close(cv.result(), r64, K, A, B, "misaligned A")
+
+
+def test_misaligned_operands_every_direct_lds_config(fg, dev, orc):
+    # A and B 4, 8 or 12 bytes past a 16-byte boundary (aligned shape and
+    # leading dimensions): the scalar variant, whose direct-LDS matrix-core
+    # kernels issue 16-byte loads at these 4-byte-aligned addresses.  NaN
+    # fills the buffers around the operands; C sits inside canaries.
+    M, N, K = 200, 256, 128
+    A, B, C = inputs.make_random(M, N, K, seed=19)
+    _, r64 = orc.sgemm(A, B, C, 0.5, 3.0)
+    cfgs = [c for c in fg.configs() if c["opt"] & 16]
+    for offa, offb in ((1, 2), (3, 1)):
+        log(f"[misaligned] A +{4 * offa} B +{4 * offb} bytes: {len(cfgs)} configs")
+        Abuf = torch.full((M * K + 8,), float("nan"), device=dev)
+        Bbuf = torch.full((K * N + 8,), float("nan"), device=dev)
+        Abuf[offa:offa + M * K] = to_dev(A.ravel(), dev)
+        Bbuf[offb:offb + K * N] = to_dev(B.ravel(), dev)
+        Aoff = Abuf[offa:offa + M * K].view(M, K)
+        Boff = Bbuf[offb:offb + K * N].view(K, N)
+        pl = fg.plan(M, N, K, Aoff.data_ptr(), K, Boff.data_ptr(), N, 1 << 40, N)
+        assert pl["vector_variant"] == 0
+        for c in cfgs:
+            cv = Canvas(C, N, 2, dev)
+            fg.sgemm_ex(Aoff, Boff, cv.view, 0.5, 3.0, cfg_id=c["id"])
+            torch.cuda.synchronize()
+            assert cv.untouched(), f"cfg {c['id']}: wrote outside C"
+            check_close(cv.result(), r64, K, A, B, f"cfg {c['id']} misaligned {offa},{offb}")
 
 
 def test_transpose_identity_bit_exact(fg, dev):
