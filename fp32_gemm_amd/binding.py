@@ -124,7 +124,10 @@ def config_info(cfg_id: int) -> dict:
 
 
 def _kernel_resources():
-    """Compiler resource report per tuple and variant, if the build left one."""
+    """Compiler resource report per tuple and kernel, if the build left one:
+    keys (tuple, "vec"), (tuple, "scalar") (the scalar variant's kernel for
+    any N) and (tuple, "scalar_b16") (its kernel for N % 4 == 0, where the
+    tuple has one of its own)."""
     if not os.path.exists(_RESOURCES):
         return {}
     with open(_RESOURCES) as f:
@@ -135,7 +138,11 @@ def _kernel_resources():
         m = pat.search(name)
         if m:
             g = tuple(int(x) for x in m.groups())
-            out[(g[:12], g[12])] = v
+            if "hyb" in name:  # the scalar variant's kernels with 16-byte A loads
+                kind = "scalar_b16" if g[12] else "scalar"
+            else:
+                kind = "vec" if g[12] else "scalar"
+            out[(g[:12], kind)] = v
     return out
 
 
@@ -145,13 +152,17 @@ def configs():
     out = []
     for i in range(num_configs()):
         d = config_info(i)
-        d["resources_vec"] = res.get((d["tuple"], 1))
-        d["resources_scalar"] = res.get((d["tuple"], 0))
+        d["resources_vec"] = res.get((d["tuple"], "vec"))
+        d["resources_scalar"] = res.get((d["tuple"], "scalar"))
+        d["resources_scalar_b16"] = res.get((d["tuple"], "scalar_b16"), d["resources_scalar"])
         out.append(d)
     return out
 
 
-def kernel_attributes(cfg_id: int, vector_variant: bool = True) -> dict:
+def kernel_attributes(cfg_id: int, vector_variant: int = 1) -> dict:
+    """Runtime attributes of a compiled kernel: vector_variant 1 the float4
+    kernel, 0 the scalar variant's kernel for any N, 2 its kernel for
+    N % 4 == 0."""
     a = _Attr()
     rc = _lib.sgemm_kernel_attributes(cfg_id, int(vector_variant), ctypes.byref(a))
     if rc != 0:

@@ -1136,15 +1136,26 @@ const void* hybrid_symbol() {
 }
 
 // The kernel of a variant (for the scalar variant of a hybrid tuple, the
-// one with 16-byte B loads; its registers and occupancy stand for both).
+// one with 4-byte B loads, which any N can run).
 template <class Cfg, bool VEC>
 const void* kernel_symbol() {
   if constexpr (!VEC && hybrid_scalar<Cfg>())
-    return hybrid_symbol<Cfg, true>();
+    return hybrid_symbol<Cfg, false>();
   else if constexpr (min_blocks_of(Cfg::tile) > 0)
     return reinterpret_cast<const void*>(&sgemm_tile_kernel_occ<Cfg, VEC>);
   else
     return reinterpret_cast<const void*>(&sgemm_tile_kernel<Cfg, VEC>);
+}
+
+// The scalar variant's kernel when N % 4 == 0: for a hybrid tuple the one
+// with 16-byte B loads (its occupancy can differ from the other's), else the
+// same kernel as for any N.
+template <class Cfg>
+const void* kernel_symbol_b16() {
+  if constexpr (hybrid_scalar<Cfg>())
+    return hybrid_symbol<Cfg, true>();
+  else
+    return kernel_symbol<Cfg, false>();
 }
 
 // Host-side launcher for one instantiated tuple and variant.
@@ -1203,8 +1214,8 @@ hipError_t launch_tile(const KernelArgs& a, hipStream_t stream, long long slots)
   const long long grid = sp.tiles_full + tail * sp.splits;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
   const void* kernel = kernel_symbol<Cfg, VEC>();
-  if constexpr (!VEC && hybrid_scalar<Cfg>()) {
-    if (a.N % 4 != 0) kernel = hybrid_symbol<Cfg, false>();
+  if constexpr (!VEC) {
+    if (a.N % 4 == 0) kernel = kernel_symbol_b16<Cfg>();
   }
   return hipLaunchKernel(kernel, dim3(static_cast<unsigned>(grid)),
                          dim3(Cfg::NT), args, 0, stream);

@@ -182,7 +182,10 @@ int sgemm_last_hip_error(void);
 int sgemm_device_check(void);
 
 /* Register/LDS/scratch use of a compiled kernel (needs a device).
- * vector_variant selects the float4 (1) or scalar (0) kernel. */
+ * vector_variant selects the float4 kernel (1), the scalar variant's kernel
+ * for any N (0), or the scalar variant's kernel for N % 4 == 0 (2; the same
+ * as 0 except for the direct-to-LDS matrix-core configurations below
+ * 256 x 256, whose scalar variant then loads B 16 bytes at a time). */
 typedef struct sgemm_kernel_attr_t {
   int32_t num_regs;       /* architectural VGPRs reported by the runtime */
   int32_t scratch_bytes;  /* private (spill) bytes per lane */

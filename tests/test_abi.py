@@ -274,6 +274,22 @@ def test_config_table_contents():
         assert c["resources_vec"] is not None and c["resources_scalar"] is not None
 
 
+def test_scalar_variant_kernels_per_tuple():
+    # Direct-LDS matrix-core tuples below 256 x 256 have two scalar-variant
+    # kernels (4-byte and 16-byte B loads) in the build's resource report;
+    # every other tuple has one, which also serves N % 4 == 0.
+    hybrid = 0
+    for c in fg.configs():
+        t = c["tuple"]
+        if t[11] & 16 and t[9] != 0 and t[0] * t[1] < 256 * 256:
+            hybrid += 1
+            assert c["resources_scalar_b16"] is not None
+            assert c["resources_scalar_b16"] is not c["resources_scalar"]
+        else:
+            assert c["resources_scalar_b16"] is c["resources_scalar"]
+    assert hybrid > 0
+
+
 def test_default_configs_do_not_spill():
     for M, N, K in [(4096, 4096, 4096), (256, 256, 256), (1024, 1024, 1024)]:
         _, p = plan(M, N, K, K, N, N)
