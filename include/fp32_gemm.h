@@ -120,7 +120,9 @@ typedef struct sgemm_config_t {
                   order, bit 2 unpinned global loads, bit 3 split-K for a partly filled
                   last wave (those tiles accumulate with fp32 atomics: not bitwise
                   reproducible), bit 4 direct global-to-LDS loads (both MFMA paths;
-                  16-byte loads in the float4 variant, 4-byte loads in the scalar one),
+                  16-byte loads in the float4 variant, 4-byte loads in the scalar one
+                  but for the 16-byte ones of tiles below 256 x 256 described at
+                  sgemm_ex),
                   bits 5-6 with bit 4: LDS stages - 2, bits 7-8: workgroups per CU
                   requested - 1 (0 = none), bit 9 k-sliced workgroup (with bit 4:
                   two wave groups of NT/2 threads split the K slices and add their
