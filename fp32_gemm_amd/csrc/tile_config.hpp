@@ -64,7 +64,9 @@ enum Opt : int {
   kOptSplitK = 8,
   // Global -> LDS with buffer loads that write LDS directly (no register
   // round-trip, no ds_write).  MFMA paths: 16-byte loads in the float4
-  // variant, 4-byte loads in the scalar variant, into an As[m][k] layout
+  // variant, 4-byte loads in the scalar variant (below 256 x 256 tiles, only
+  // for slice 0's A and, when N % 4 != 0, for B: hybrid_scalar_tile), into
+  // an As[m][k] layout
   // whose 16-byte chunks are XOR-swizzled by row; the inner product reads
   // four k of A per 128-bit LDS read.  VALU path: A keeps the transposed,
   // swizzled As[k][m] layout of register staging, filled by 4-byte loads (each
