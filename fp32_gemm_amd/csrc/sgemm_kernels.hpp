@@ -1101,15 +1101,13 @@ __global__ void __launch_bounds__(Cfg::NT)
   tile_body<Cfg, VEC>(p);
 }
 
-// The scalar variant of a direct-LDS matrix-core tuple below 256 x 256
-// (hybrid_scalar_tile): 16-byte buffer loads need only 4-byte alignment, and
+// The scalar variant of a direct-LDS matrix-core tuple (hybrid_scalar_tile):
+// 16-byte buffer loads need only 4-byte alignment, and
 // every K slice after the first is whole, so A loads 16 bytes per lane in
 // those slices whatever K, lda or the operand's alignment; only slice 0,
 // when K % 4 != 0, loads A 4 bytes per lane.  B loads 16 bytes per lane when
 // N % 4 == 0 (BV) and 4 otherwise (a float4 would straddle column N).  The
-// matrix-core epilogue stores element by element either way.  (The 256 x 256
-// tuples keep the plain scalar kernel: with 4-byte B loads their registers
-// overflow.)
+// matrix-core epilogue stores element by element either way.
 template <class Cfg>
 constexpr bool hybrid_scalar() {
   return hybrid_scalar_tile(Cfg::tile);

@@ -64,9 +64,8 @@ enum Opt : int {
   kOptSplitK = 8,
   // Global -> LDS with buffer loads that write LDS directly (no register
   // round-trip, no ds_write).  MFMA paths: 16-byte loads in the float4
-  // variant, 4-byte loads in the scalar variant (below 256 x 256 tiles, only
-  // for slice 0's A and, when N % 4 != 0, for B: hybrid_scalar_tile), into
-  // an As[m][k] layout
+  // variant, 4-byte loads in the scalar variant (only for slice 0's A and,
+  // when N % 4 != 0, for B: hybrid_scalar_tile), into an As[m][k] layout
   // whose 16-byte chunks are XOR-swizzled by row; the inner product reads
   // four k of A per 128-bit LDS read.  VALU path: A keeps the transposed,
   // swizzled As[k][m] layout of register staging, filled by 4-byte loads (each
@@ -99,11 +98,10 @@ enum Opt : int {
 constexpr int stages_of(const Tile& t) { return 2 + ((t.opt & kOptStagesMask) >> kOptStagesShift); }
 
 // Tuples whose scalar variant keeps 16-byte loads for A (after the first K
-// slice) and for B when N % 4 == 0: direct-LDS matrix-core tiles below
-// 256 x 256 (the kernels' hybrid scalar body; with 4-byte B loads the
-// registers of the larger tiles overflow).
+// slice) and for B when N % 4 == 0: the direct-LDS matrix-core tiles (the
+// kernels' hybrid scalar body).
 constexpr bool hybrid_scalar_tile(const Tile& t) {
-  return (t.opt & kOptDirectLds) != 0 && t.path != kPathValu && t.BM * t.BN < 256 * 256;
+  return (t.opt & kOptDirectLds) != 0 && t.path != kPathValu;
 }
 
 // Wave groups a k-sliced tuple splits its K loop over (1 otherwise), and the

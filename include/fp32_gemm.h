@@ -78,9 +78,8 @@ int sgemm(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64_t 
  * the tuned choice when cfg_id < 0.  Operands that are not 16-byte aligned,
  * whose leading dimensions are not multiples of 4, or with K or N not a
  * multiple of 4 run the scalar-load variant of the same configuration.  In
- * that variant the direct-to-LDS matrix-core configurations below 256 x 256
- * still load A 16 bytes at a time after the first K slice, and B too when
- * N % 4 == 0. */
+ * that variant the direct-to-LDS matrix-core configurations still load A 16
+ * bytes at a time after the first K slice, and B too when N % 4 == 0. */
 int sgemm_ex(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64_t lda,
              const float* B, int64_t ldb, float beta, float* C, int64_t ldc, void* stream,
              int32_t cfg_id);
@@ -121,8 +120,7 @@ typedef struct sgemm_config_t {
                   last wave (those tiles accumulate with fp32 atomics: not bitwise
                   reproducible), bit 4 direct global-to-LDS loads (both MFMA paths;
                   16-byte loads in the float4 variant, 4-byte loads in the scalar one
-                  but for the 16-byte ones of tiles below 256 x 256 described at
-                  sgemm_ex),
+                  but for the 16-byte ones described at sgemm_ex),
                   bits 5-6 with bit 4: LDS stages - 2, bits 7-8: workgroups per CU
                   requested - 1 (0 = none), bit 9 k-sliced workgroup (with bit 4:
                   two wave groups of NT/2 threads split the K slices and add their
@@ -186,8 +184,8 @@ int sgemm_device_check(void);
 /* Register/LDS/scratch use of a compiled kernel (needs a device).
  * vector_variant selects the float4 kernel (1), the scalar variant's kernel
  * for any N (0), or the scalar variant's kernel for N % 4 == 0 (2; the same
- * as 0 except for the direct-to-LDS matrix-core configurations below
- * 256 x 256, whose scalar variant then loads B 16 bytes at a time). */
+ * as 0 except for the direct-to-LDS matrix-core configurations, whose
+ * scalar variant then loads B 16 bytes at a time). */
 typedef struct sgemm_kernel_attr_t {
   int32_t num_regs;       /* architectural VGPRs reported by the runtime */
   int32_t scratch_bytes;  /* private (spill) bytes per lane */

@@ -201,14 +201,14 @@ def test_off_rule_shapes_follow_the_rate_table():
     # exp(-squared distance) * log(percentage / 100); a shape that is a row
     # takes that row's fastest column.  Float4 shapes read the float4 rows;
     # scalar-variant shapes with N % 4 == 0 read them too, among the tiles
-    # whose scalar kernel keeps 16-byte loads (direct-LDS matrix-core tiles
-    # below 256 x 256); other scalar-variant shapes read the scalar rows.
+    # whose scalar kernel keeps 16-byte loads (direct-LDS matrix-core
+    # tiles); other scalar-variant shapes read the scalar rows.
     # The choice needs no device, so this holds on any host.
     cols, scalar, vector = _rate_table()
     rules = _table_rules()
 
     def hybrid(t):
-        return bool(t[11] & 16) and t[9] != 0 and t[0] * t[1] < 256 * 256
+        return bool(t[11] & 16) and t[9] != 0
 
     def expected(M, N, K, vec):
         b16 = not vec and N % 4 == 0
@@ -275,13 +275,13 @@ def test_config_table_contents():
 
 
 def test_scalar_variant_kernels_per_tuple():
-    # Direct-LDS matrix-core tuples below 256 x 256 have two scalar-variant
-    # kernels (4-byte and 16-byte B loads) in the build's resource report;
-    # every other tuple has one, which also serves N % 4 == 0.
+    # Direct-LDS matrix-core tuples have two scalar-variant kernels (4-byte
+    # and 16-byte B loads) in the build's resource report; every other tuple
+    # has one, which also serves N % 4 == 0.
     hybrid = 0
     for c in fg.configs():
         t = c["tuple"]
-        if t[11] & 16 and t[9] != 0 and t[0] * t[1] < 256 * 256:
+        if t[11] & 16 and t[9] != 0:
             hybrid += 1
             assert c["resources_scalar_b16"] is not None
             assert c["resources_scalar_b16"] is not c["resources_scalar"]
