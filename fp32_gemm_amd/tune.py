@@ -419,6 +419,109 @@ def write_rate_table(records, path, command):
     return cols, counts[False], counts[True]
 
 
+_RATE_ROW = re.compile(r"^(\s*)\{(\d+), (\d+), (\d+), \{([\d, ]+)\}\},\s*// best ([\d.]+) TFLOP/s$")
+
+
+def read_rate_table(path):
+    """The columns of a measured-rate table (tuples) and its rows per
+    variant: {"scalar": [(M, N, K, pcts)], "vector": [...]}."""
+    cols, rows, kind = [], {"scalar": [], "vector": []}, None
+    for line in open(path):
+        if "// column" in line:
+            cols.append(tuple(int(x) for x in line.split("{")[1].split("}")[0].split(",")))
+        elif "kScalarRows[]" in line:
+            kind = "scalar"
+        elif "kVectorRows[]" in line:
+            kind = "vector"
+        else:
+            m = _RATE_ROW.match(line.rstrip("\n"))
+            if m and kind:
+                rows[kind].append((int(m.group(2)), int(m.group(3)), int(m.group(4)),
+                                   [int(x) for x in m.group(5).split(", ")]))
+    return cols, rows
+
+
+def retime_rate_column(dev, path, column, kind="scalar"):
+    """Re-times one column of the measured-rate table on every row of one
+    variant, beside the row's fastest other column, with the off-table
+    studies' protocol (A, B, C ~ N(0,1), beta = 0; 3 warm-up launches each,
+    then 6 rounds of one 3-launch batch of each in turn).  For a column
+    whose kernel changed since the table was measured.  Scalar rows with
+    N % 4 == 0 are skipped: such shapes run the scalar kernels with 16-byte
+    B loads, while the dispatch reads the scalar rows only for N % 4 != 0.
+    Returns {(M, N, K): (column rate, anchor column, anchor rate)} in
+    TFLOP/s."""
+    cols, rows = read_rate_table(path)
+    ids = {c["tuple"]: c["id"] for c in fg.configs()}
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    for M, N, K, pct in rows[kind]:
+        if kind == "scalar" and N % 4 == 0:
+            continue
+        anchor = max((j for j in range(len(cols)) if j != column), key=lambda j: pct[j])
+        A = torch.randn(M, K, device=dev)
+        B = torch.randn(K, N, device=dev)
+        C = torch.randn(M, N, device=dev)
+        fns = [lambda c=ids[cols[j]]: fg.sgemm_ex(A, B, C, 1.0, 0.0, stream=stream, cfg_id=c)
+               for j in (column, anchor)]
+        for f in fns:
+            for _ in range(3):
+                f()
+        samples = [[], []]
+        for _ in range(6):
+            for i, f in enumerate(fns):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(3):
+                    f()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                samples[i].append(e0.elapsed_time(e1) / 3)
+        r = [model.flops(M, N, K) / (float(np.median(v)) * 1e-3) / 1e12 for v in samples]
+        out[(M, N, K)] = (round(r[0], 2), anchor, round(r[1], 2))
+        print(f"[rate-column] {M}x{N}x{K} column {column} {r[0]:.1f}, column {anchor} {r[1]:.1f}",
+              flush=True)
+    return out
+
+
+def refresh_rate_column(path, column, kind, retimed, command):
+    """Rewrites the rows of one variant that `retimed` covers: the column's
+    percentage becomes its new rate over its anchor column's, both timed
+    side by side, times the anchor's stored percentage; where that passes
+    100 the row is rescaled so that its fastest column is 100 again (every
+    percentage at least 1).  The other columns keep their ratios, and the
+    command joins the table's header.  Scalar rows with N % 4 == 0 are left
+    as they are, as retime_rate_column skips them.  Returns the rows whose
+    fastest column changed."""
+    lines = open(path).read().split("\n")
+    out, cur, moved = [], None, []
+    for line in lines:
+        if "kScalarRows[]" in line:
+            cur = "scalar"
+        elif "kVectorRows[]" in line:
+            cur = "vector"
+        m = _RATE_ROW.match(line)
+        key = tuple(int(m.group(i)) for i in (2, 3, 4)) if m else None
+        if m and cur == kind and key in retimed and not (kind == "scalar" and key[1] % 4 == 0):
+            pct = [int(x) for x in m.group(5).split(", ")]
+            rate, anchor, anchor_rate = retimed[key]
+            rel = [float(x) for x in pct]
+            rel[column] = pct[anchor] * rate / anchor_rate
+            top = max(rel)
+            new = [max(1, int(round(100.0 * x / top))) for x in rel]
+            if new.index(100) != pct.index(100):
+                moved.append(key)
+            best = float(m.group(6)) * top / 100.0
+            line = "%s{%d, %d, %d, {%s}},  // best %.1f TFLOP/s" % (
+                m.group(1), *key, ", ".join(map(str, new)), best)
+        out.append(line)
+    at = next(i for i, l in enumerate(out) if l.startswith("// Tile order"))
+    out[at:at] = [f"// Column {column} of the {kind} rows re-timed by `{command}`"]
+    with open(path, "w") as f:
+        f.write("\n".join(out))
+    return moved
+
+
 def write_rate_table_gap(swept, path, command):
     """Markdown table: per swept shape, the fastest of every swept tuple
     against the fastest tile of the measured-rate table (short protocol)."""
@@ -562,7 +665,25 @@ def main():
                     help="write --rate-table-out from these off-table records (comma-separated "
                          "JSONL files of --off-table runs); no GPU needed")
     ap.add_argument("--rate-table-out", default=None)
+    ap.add_argument("--rate-column", type=int, default=None, metavar="COLUMN",
+                    help="re-time this column of csrc/measured_rates.inc on the --rate-kind rows "
+                         "beside each row's fastest other column; writes --out")
+    ap.add_argument("--rate-kind", default="scalar", choices=("scalar", "vector"))
+    ap.add_argument("--rate-retimed", default=None, metavar="FILE",
+                    help="with --rate-column: rewrite those rows of csrc/measured_rates.inc from "
+                         "this --out file of a --rate-column run; no GPU needed")
     args = ap.parse_args()
+    if args.rate_column is not None and args.rate_retimed:
+        path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", "measured_rates.inc")
+        retimed = {(r["M"], r["N"], r["K"]): (r["rate"], r["anchor"], r["anchor_rate"])
+                   for r in map(json.loads, open(args.rate_retimed)) if r}
+        moved = refresh_rate_column(path, args.rate_column, args.rate_kind, retimed,
+                                    f"python -m fp32_gemm_amd.tune --rate-column {args.rate_column} "
+                                    f"--rate-kind {args.rate_kind} --out "
+                                    f"{os.path.basename(args.rate_retimed)}")
+        print(f"[rate-column] {len(retimed)} re-timed rows read, {len(moved)} rows with a new fastest "
+              "column")
+        return 0
     if args.rate_table:
         recs = [json.loads(l) for f in args.rate_table.split(",") for l in open(f) if l.strip()]
         # The command as written into the table names the record files
@@ -583,6 +704,13 @@ def main():
     torch.cuda.set_device(dev)
     if fg.device_check() != 0:
         raise SystemExit("tune: current device is not gfx950")
+    if args.rate_column is not None:
+        path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", "measured_rates.inc")
+        retimed = retime_rate_column(dev, path, args.rate_column, args.rate_kind)
+        with open(args.out, "w") as f:
+            for (M, N, K), (r, j, rj) in retimed.items():
+                f.write(json.dumps(dict(M=M, N=N, K=K, rate=r, anchor=j, anchor_rate=rj)) + "\n")
+        return 0
     if args.off_table is not None:
         off_table(args.off_table, dev, args.out, args.summary_out,
                   "python -m fp32_gemm_amd.tune " + " ".join(sys.argv[1:]), aligned=args.aligned,

@@ -84,3 +84,43 @@ def test_rate_table_gap_summary(tmp_path):
     tune.write_rate_table_gap(swept, str(path), "cmd")
     row = [l for l in path.read_text().split("\n") if l.startswith("| 100x200x300")][0]
     assert "| 1,2,3 | 50.0 |" in row and f"| {','.join(map(str, in_table))} | 40.0 | 0.800 |" in row
+
+
+def test_rate_column_refresh(tmp_path):
+    # A re-timed column takes its rate over its anchor's, times the anchor's
+    # stored percentage; a column that now leads rescales the row to 100.
+    # Rows of the other variant and rows not re-timed stay as they were.
+    a, b, c = "64,64,16,32,32,1,16,1,256,1,32,18", "128,128,16,64,64,4,4,1,256,2,64,24", \
+        "256,256,32,128,64,2,16,1,512,1,32,27"
+    recs = [
+        dict(M=1000, N=1001, K=999, vec=False, rates={a: 50.0, b: 100.0, c: 20.0}),
+        dict(M=2000, N=2001, K=1999, vec=False, rates={a: 80.0, b: 40.0, c: 10.0}),
+        dict(M=3000, N=3001, K=2999, vec=False, rates={a: 80.0, b: 40.0, c: 10.0}),
+        dict(M=512, N=512, K=512, vec=True, rates={a: 1.0, b: 2.0, c: 1.0}),
+    ]
+    path = tmp_path / "rates.inc"
+    tune.write_rate_table(recs, str(path), "cmd")
+    cols, rows = tune.read_rate_table(str(path))
+    assert [",".join(map(str, t)) for t in cols] == [a, b, c]
+    assert rows["scalar"][1] == (2000, 2001, 1999, [100, 50, 12])
+    assert rows["vector"] == [(512, 512, 512, [50, 100, 50])]
+    # Row 1: column 2 at 0.6 of its anchor (column 1, 100 %) -> 60.
+    # Row 2: column 2 at 1.5x its anchor (column 0, 100 %) -> leads; the
+    # others scale by 1/1.5 and the best rate by 1.5.
+    moved = tune.refresh_rate_column(str(path), 2, "scalar",
+                                     {(1000, 1001, 999): (60.0, 1, 100.0),
+                                      (2000, 2001, 1999): (150.0, 0, 100.0)}, "recmd")
+    assert moved == [(2000, 2001, 1999)]
+    cols2, rows2 = tune.read_rate_table(str(path))
+    assert cols2 == cols
+    assert rows2["scalar"][0][3] == [50, 100, 60]
+    assert rows2["scalar"][1][3] == [67, 33, 100]
+    assert rows2["scalar"][2] == rows["scalar"][2] and rows2["vector"] == rows["vector"]
+    text = path.read_text()
+    assert "{2000, 2001, 1999, {67, 33, 100}},  // best 120.0 TFLOP/s" in text
+    assert "// Column 2 of the scalar rows re-timed by `recmd`" in text
+    # A scalar row with N % 4 == 0 is not rewritten.
+    recs[2]["N"] = 3000
+    tune.write_rate_table(recs, str(path), "cmd")
+    tune.refresh_rate_column(str(path), 2, "scalar", {(3000, 3000, 2999): (150.0, 0, 100.0)}, "x")
+    assert tune.read_rate_table(str(path))[1]["scalar"][2] == (3000, 3000, 2999, [100, 50, 12])
