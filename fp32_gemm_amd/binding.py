@@ -125,24 +125,21 @@ def config_info(cfg_id: int) -> dict:
 
 def _kernel_resources():
     """Compiler resource report per tuple and kernel, if the build left one:
-    keys (tuple, "vec"), (tuple, "scalar") (the scalar variant's kernel for
-    any N) and (tuple, "scalar_b16") (its kernel for N % 4 == 0, where the
-    tuple has one of its own)."""
+    keys (tuple, "vec") and (tuple, "scalar")."""
     if not os.path.exists(_RESOURCES):
         return {}
     with open(_RESOURCES) as f:
         raw = json.load(f)
     out = {}
-    pat = re.compile(r"TileCfgILi" + r"ELi".join([r"(\d+)"] * 12) + r"EEELb(\d)")
+    pat = re.compile(r"TileCfgILi" + r"ELi".join([r"(\d+)"] * 12) + r"EEE(?:Lb(\d))?")
     for name, v in raw.items():
         m = pat.search(name)
         if m:
-            g = tuple(int(x) for x in m.groups())
-            if "hyb" in name:  # the scalar variant's kernels with 16-byte A loads
-                kind = "scalar_b16" if g[12] else "scalar"
-            else:
-                kind = "vec" if g[12] else "scalar"
-            out[(g[:12], kind)] = v
+            g = tuple(int(x) for x in m.groups()[:12])
+            # The hybrid kernels (the scalar variant of direct-LDS matrix-core
+            # tuples) take no variant flag.
+            kind = "scalar" if "hyb" in name or m.group(13) == "0" else "vec"
+            out[(g, kind)] = v
     return out
 
 
@@ -154,15 +151,13 @@ def configs():
         d = config_info(i)
         d["resources_vec"] = res.get((d["tuple"], "vec"))
         d["resources_scalar"] = res.get((d["tuple"], "scalar"))
-        d["resources_scalar_b16"] = res.get((d["tuple"], "scalar_b16"), d["resources_scalar"])
         out.append(d)
     return out
 
 
 def kernel_attributes(cfg_id: int, vector_variant: int = 1) -> dict:
     """Runtime attributes of a compiled kernel: vector_variant 1 the float4
-    kernel, 0 the scalar variant's kernel for any N, 2 its kernel for
-    N % 4 == 0."""
+    kernel, 0 the scalar variant's."""
     a = _Attr()
     rc = _lib.sgemm_kernel_attributes(cfg_id, int(vector_variant), ctypes.byref(a))
     if rc != 0:

@@ -196,12 +196,12 @@ __device__ __forceinline__ int slice_k0(int kt, int r, int BK) {
 // kMaxBufferBytes (lda, ldb >= K, N and at most kMaxLeadingDim; BM, BK <=
 // kMaxTileRows), so they fit in 32 bits.
 //
-// VA / VB: 16-byte loads for A / B (4-byte loads otherwise); the two differ
-// only in the scalar variant's hybrid kernels (tile_body).
-template <class Cfg, bool VA, bool VB = VA>
+// VA: 16-byte loads for both operands (4-byte loads otherwise); the hybrid
+// kernels' first K slice loads A 4 bytes per lane (dma_first_slice's A1S).
+template <class Cfg, bool VA>
 struct DmaLanes {
   static constexpr Geom g = make_geom(Cfg::tile);
-  static constexpr int FPL = VB ? 4 : 1;
+  static constexpr int FPL = VA ? 4 : 1;
   // The VALU path loads its transposed A 4 bytes per lane in both variants.
   static constexpr int FPL_A = Cfg::PATH == kPathValu ? 1 : VA ? 4 : 1;
   int a_off[dma_ops_a(g, FPL_A)];
@@ -211,11 +211,11 @@ struct DmaLanes {
   int a_ext, b_ext;
 };
 
-template <class Cfg, bool VA, bool VB = VA>
+template <class Cfg, bool VA>
 __device__ __forceinline__ void dma_setup(const KernelArgs& p, int row0, int col0, int wave,
-                                          int lane, DmaLanes<Cfg, VA, VB>& d) {
+                                          int lane, DmaLanes<Cfg, VA>& d) {
   constexpr Geom g = make_geom(Cfg::tile);
-  constexpr int FPL = DmaLanes<Cfg, VA, VB>::FPL, FPL_A = DmaLanes<Cfg, VA, VB>::FPL_A;
+  constexpr int FPL = DmaLanes<Cfg, VA>::FPL, FPL_A = DmaLanes<Cfg, VA>::FPL_A;
   static_assert(g.BM <= kMaxTileRows && g.BK <= kMaxTileRows, "resource extents need 32 bits");
   const int lda = static_cast<int>(p.lda), ldb = static_cast<int>(p.ldb);
   const int cols = p.N - col0;
@@ -233,7 +233,8 @@ __device__ __forceinline__ void dma_setup(const KernelArgs& p, int row0, int col
 #pragma unroll
   for (int j = 0; j < dma_ops_b(g, FPL); ++j) {
     const KN s = dma_b_src(g, dma_op(g, wave, j), lane, FPL);
-    // With 16-byte B loads N % 4 == 0: a float4 is wholly inside or outside.
+    // A float4 that starts before column N may cross it; what it brings past
+    // N feeds only outputs the epilogue never stores.
     d.b_off[j] = s.n < cols ? (s.k * ldb + s.n) * 4 : kMaskedOffset;
   }
 }
@@ -251,11 +252,11 @@ __device__ __forceinline__ void dma_load(__amdgpu_buffer_rsrc_t r, float* dst, i
 // zeros): part PART of PARTS, the wave's A instructions followed by its B
 // instructions cut into PARTS consecutive runs.  Completion is waited for
 // with vmcnt before the barrier that publishes the stage.
-template <class Cfg, bool VA, int PART = 0, int PARTS = 1, bool VB = VA>
-__device__ __forceinline__ void dma_slice(const KernelArgs& p, const DmaLanes<Cfg, VA, VB>& d,
+template <class Cfg, bool VA, int PART = 0, int PARTS = 1>
+__device__ __forceinline__ void dma_slice(const KernelArgs& p, const DmaLanes<Cfg, VA>& d,
                                           float* stage, int k0, int wave) {
   constexpr Geom g = make_geom(Cfg::tile);
-  constexpr int FPL = DmaLanes<Cfg, VA, VB>::FPL, FPL_A = DmaLanes<Cfg, VA, VB>::FPL_A;
+  constexpr int FPL = DmaLanes<Cfg, VA>::FPL, FPL_A = DmaLanes<Cfg, VA>::FPL_A;
   constexpr int NA = dma_ops_a(g, FPL_A), NB = dma_ops_b(g, FPL);
   constexpr int U0 = PART * (NA + NB) / PARTS, U1 = (PART + 1) * (NA + NB) / PARTS;
   const int kr = p.K - k0;
@@ -274,7 +275,7 @@ __device__ __forceinline__ void dma_slice(const KernelArgs& p, const DmaLanes<Cf
     const auto rb = make_rsrc_exact(d.b_col + static_cast<long long>(k0) * p.ldb, d.b_ext & live);
 #pragma unroll
     for (int j = (U0 > NA ? U0 : NA) - NA; j < U1 - NA; ++j)
-      dma_load<VB>(rb, stage + g.BM * g.BK + dma_op(g, wave, j) * 64 * FPL, d.b_off[j]);
+      dma_load<VA>(rb, stage + g.BM * g.BK + dma_op(g, wave, j) * 64 * FPL, d.b_off[j]);
   }
 }
 
@@ -314,11 +315,11 @@ __device__ __forceinline__ void dma_c_band(const KernelArgs& p, float* stage, in
 // valid term).  In the float4 variant r % 4 == 0, so a float4 is wholly
 // inside or outside.  With A1S the A part loads 4 bytes per lane (the same
 // LDS layout), so r need not be a multiple of 4.
-template <class Cfg, bool VA, bool A1S = false, bool VB = VA>
+template <class Cfg, bool VA, bool A1S = false>
 __device__ __forceinline__ void dma_first_slice(const KernelArgs& p, float* stage, int row0,
                                                 int col0, int r, int wave, int lane) {
   constexpr Geom g = make_geom(Cfg::tile);
-  constexpr int FPL = VB ? 4 : 1;
+  constexpr int FPL = VA ? 4 : 1;
   constexpr int FPL_A = Cfg::PATH == kPathValu || A1S ? 1 : VA ? 4 : 1;
   const int lda = static_cast<int>(p.lda), ldb = static_cast<int>(p.ldb);
   const int rows = min(g.BM, p.M - row0);
@@ -336,7 +337,7 @@ __device__ __forceinline__ void dma_first_slice(const KernelArgs& p, float* stag
 #pragma unroll
   for (int j = 0; j < dma_ops_b(g, FPL); ++j) {
     const KN s = dma_b_src(g, dma_op(g, wave, j), lane, FPL);
-    dma_load<VB>(rb, stage + g.BM * g.BK + dma_op(g, wave, j) * 64 * FPL,
+    dma_load<VA>(rb, stage + g.BM * g.BK + dma_op(g, wave, j) * 64 * FPL,
                  s.k < r && s.n < p.N - col0 ? (s.k * ldb + s.n) * 4 : kMaskedOffset);
   }
 }
@@ -825,14 +826,14 @@ __device__ __forceinline__ void acc_add(Acc<Cfg>& acc, int e, float x) {
 // The body of the tile kernel (one workgroup, one output tile or K segment).
 // HYB (scalar variant of a direct-LDS matrix-core tuple, VEC false): 16-byte
 // loads for A in every slice but the first, which loads A 4 bytes per lane,
-// and for B if HBV (N % 4 == 0); see sgemm_tile_kernel_hyb.
-template <class Cfg, bool VEC, bool HYB = false, bool HBV = false>
+// and for B in every slice; see sgemm_tile_kernel_hyb.
+template <class Cfg, bool VEC, bool HYB = false>
 __device__ __forceinline__ void tile_body(const KernelArgs& p) {
   constexpr Geom g = make_geom(Cfg::tile);
   static_assert(tile_legal(Cfg::tile), "illegal tile tuple instantiated");
   constexpr bool kDirect = (Cfg::OPT & kOptDirectLds) != 0;
   static_assert(!HYB || (!VEC && kDirect && Cfg::PATH != kPathValu), "hybrid body: direct-LDS MFMA, scalar variant");
-  constexpr bool VA = VEC || HYB, VB = VEC || (HYB && HBV);
+  constexpr bool VA = VEC || HYB;
   constexpr int kStages = kDirect ? stages_of(Cfg::tile) : 2;
   // K-sliced tuples: two wave groups, each with its own LDS ring, run the K
   // loop over the two halves of the slice range with the geometry of half
@@ -901,17 +902,16 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
     // past K load nothing (zeros); past a segment's end they load the next
     // segment's slices, which no one reads.
     constexpr int S = kStages;
-    constexpr int kInFlight = (S - 2) * (VA == VB ? dma_ops_per_slice(L::tile, VA ? 4 : 1)
-                                                  : dma_ops_a(lg, 4) + dma_ops_b(lg, 1));
+    constexpr int kInFlight = (S - 2) * dma_ops_per_slice(L::tile, VA ? 4 : 1);
     const int r = tail_width(p, lg.BK);
-    DmaLanes<L, VA, VB> d;
-    dma_setup<L, VA, VB>(p, row0, col0, wave, lane, d);
+    DmaLanes<L, VA> d;
+    dma_setup<L, VA>(p, row0, col0, wave, lane, d);
 #pragma unroll
     for (int i = 0; i < S - 1; ++i) {
       if (i == 0 && kt0 == 0)
-        dma_first_slice<L, VA, HYB, VB>(p, lds + ro, row0, col0, r, wave, lane);
+        dma_first_slice<L, VA, HYB>(p, lds + ro, row0, col0, r, wave, lane);
       else
-        dma_slice<L, VA, 0, 1, VB>(p, d, lds + ro + i * lg.STAGE, slice_k0(kt0 + i, r, lg.BK), wave);
+        dma_slice<L, VA>(p, d, lds + ro + i * lg.STAGE, slice_k0(kt0 + i, r, lg.BK), wave);
     }
     ring_barrier<kInFlight>();
     int cur = 0, nxt = S - 1;
@@ -933,18 +933,18 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
       // per tile, C read after it, most of all when C is not in the caches);
       // on 64-row tiles the one-at-a-time tail it needs costs more than it
       // saves.
-      constexpr bool kCPrefetch = VA && VB && S == 2 &&
+      constexpr bool kCPrefetch = VA && S == 2 &&
                                   ((L::PATH == kPathMfma32 && lg.BM * lg.BN >= 256 * 256) ||
                                    lg.BM * lg.BN == 128 * 128);
       // MFMAs per k-group and the wave's direct-to-LDS loads per slice:
       // where the group after the barrier has two MFMAs or more per load,
       // the loads are spread over it.
       constexpr int kMf = 4 * lg.WMITER * lg.WNITER;
-      constexpr int kVm = dma_ops_a(lg, VA ? 4 : 1) + dma_ops_b(lg, VB ? 4 : 1);
+      constexpr int kVm = dma_ops_a(lg, VA ? 4 : 1) + dma_ops_b(lg, VA ? 4 : 1);
       constexpr bool kSpread = kMf >= 2 * kVm;
       DmaFrag<L> f[2];
       dma_frag_load<L>(lds + ro, 0, wr0, wc0, lane, f[0]);
-      dma_slice<L, VA, 0, 1, VB>(p, d, lds + ro + (S - 1) * lg.STAGE, slice_k0(kt0 + S - 1, r, lg.BK), wave);
+      dma_slice<L, VA>(p, d, lds + ro + (S - 1) * lg.STAGE, slice_k0(kt0 + S - 1, r, lg.BK), wave);
       // Drain the LDS queue once before the loop: entering it with other
       // LDS work possibly pending makes the compiler wait for every LDS read
       // (lgkmcnt(0)) at the head of each iteration instead of only for the
@@ -974,15 +974,15 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
           if (c_band)
             dma_c_band<L>(p, lds + ro + cs * lg.STAGE, row0 + wr0, col0 + wc0, kt + S - kt1, wave, lane);
           else
-            dma_slice<L, VA, 0, 1, VB>(p, d, lds + ro + cs * lg.STAGE, slice_k0(kt + S, r, lg.BK), wave);
+            dma_slice<L, VA>(p, d, lds + ro + cs * lg.STAGE, slice_k0(kt + S, r, lg.BK), wave);
         } else {
-          dma_slice<L, VA, 0, 1, VB>(p, d, lds + ro + cs * lg.STAGE, slice_k0(kt + S, r, lg.BK), wave);
+          dma_slice<L, VA>(p, d, lds + ro + cs * lg.STAGE, slice_k0(kt + S, r, lg.BK), wave);
         }
         dma_frag_mfma<L>(f[(KG - 1) & 1], acc);
         if constexpr (kSpread) spread_loads<kMf, kVm>();
         if constexpr ((KG & 1) != 0) f[0] = f[1];
       };
-      if constexpr (S == 2 && VA && VB && kCPrefetch) {
+      if constexpr (S == 2 && VA && kCPrefetch) {
         int kt = kt0;
         // Pairs while both slices still load real data; the last two or
         // three slices run one at a time, and those past the segment's end
@@ -992,7 +992,7 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
           slice(kt + 1, 1);
         }
         for (; kt < kt1; ++kt) slice(kt, (kt - kt0) & 1, kt + S >= kt1);
-      } else if constexpr (S == 2 && VA && VB) {
+      } else if constexpr (S == 2 && VA) {
         int kt = kt0;
         for (; kt + 1 < kt1; kt += 2) {
           slice(kt, 0);
@@ -1007,7 +1007,7 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
       }
     } else {
       auto slice = [&](int kt, int cs, int ns) __attribute__((always_inline)) {
-        dma_slice<L, VA, 0, 1, VB>(p, d, lds + ro + ns * lg.STAGE, slice_k0(kt + S - 1, r, lg.BK), wave);
+        dma_slice<L, VA>(p, d, lds + ro + ns * lg.STAGE, slice_k0(kt + S - 1, r, lg.BK), wave);
         if constexpr (!(L::OPT & kOptFloatLoads)) __builtin_amdgcn_sched_barrier(0);
         // The VALU path reads its transposed A and Bs as register staging
         // lays them out; the MFMA paths read the [m][k] chunk layout.
@@ -1017,7 +1017,7 @@ __device__ __forceinline__ void tile_body(const KernelArgs& p) {
           inner_product_dma<L>(lds + ro + cs * lg.STAGE, wr0, wc0, lane, acc);
         ring_barrier<kInFlight>();
       };
-      if constexpr (S == 2 && VA && VB) {
+      if constexpr (S == 2 && VA) {
         int kt = kt0;
         for (; kt + 1 < kt1; kt += 2) {
           slice(kt, 0, 1);
@@ -1105,56 +1105,49 @@ __global__ void __launch_bounds__(Cfg::NT)
 // 16-byte buffer loads need only 4-byte alignment, and
 // every K slice after the first is whole, so A loads 16 bytes per lane in
 // those slices whatever K, lda or the operand's alignment; only slice 0,
-// when K % 4 != 0, loads A 4 bytes per lane.  B loads 16 bytes per lane when
-// N % 4 == 0 (BV) and 4 otherwise (a float4 would straddle column N).  The
-// matrix-core epilogue stores element by element either way.
+// when K % 4 != 0, loads A 4 bytes per lane.  B loads 16 bytes per lane
+// whatever N: a float4 that starts before column N and crosses it brings the
+// row's padding or the next row's first values (zeros past the resource's
+// end) into LDS columns at or past N, and those feed only outputs at or past
+// column N, which the epilogue never stores; the matrix-core epilogue stores
+// element by element.
 template <class Cfg>
 constexpr bool hybrid_scalar() {
   return hybrid_scalar_tile(Cfg::tile);
 }
 
-template <class Cfg, bool BV>
+template <class Cfg>
 __global__ void __launch_bounds__(Cfg::NT) sgemm_tile_kernel_hyb(KernelArgs p) {
-  tile_body<Cfg, false, true, BV>(p);
+  tile_body<Cfg, false, true>(p);
 }
 
-template <class Cfg, bool BV>
+template <class Cfg>
 __global__ void __launch_bounds__(Cfg::NT)
     __attribute__((amdgpu_waves_per_eu(waves_per_eu_of(Cfg::tile))))
     sgemm_tile_kernel_hyb_occ(KernelArgs p) {
-  tile_body<Cfg, false, true, BV>(p);
+  tile_body<Cfg, false, true>(p);
 }
 
-template <class Cfg, bool BV>
+template <class Cfg>
 const void* hybrid_symbol() {
   if constexpr (min_blocks_of(Cfg::tile) > 0)
-    return reinterpret_cast<const void*>(&sgemm_tile_kernel_hyb_occ<Cfg, BV>);
+    return reinterpret_cast<const void*>(&sgemm_tile_kernel_hyb_occ<Cfg>);
   else
-    return reinterpret_cast<const void*>(&sgemm_tile_kernel_hyb<Cfg, BV>);
+    return reinterpret_cast<const void*>(&sgemm_tile_kernel_hyb<Cfg>);
 }
 
 // The kernel of a variant (for the scalar variant of a hybrid tuple, the
-// one with 4-byte B loads, which any N can run).
+// hybrid kernel).
 template <class Cfg, bool VEC>
 const void* kernel_symbol() {
   if constexpr (!VEC && hybrid_scalar<Cfg>())
-    return hybrid_symbol<Cfg, false>();
+    return hybrid_symbol<Cfg>();
   else if constexpr (min_blocks_of(Cfg::tile) > 0)
     return reinterpret_cast<const void*>(&sgemm_tile_kernel_occ<Cfg, VEC>);
   else
     return reinterpret_cast<const void*>(&sgemm_tile_kernel<Cfg, VEC>);
 }
 
-// The scalar variant's kernel when N % 4 == 0: for a hybrid tuple the one
-// with 16-byte B loads (its occupancy can differ from the other's), else the
-// same kernel as for any N.
-template <class Cfg>
-const void* kernel_symbol_b16() {
-  if constexpr (hybrid_scalar<Cfg>())
-    return hybrid_symbol<Cfg, true>();
-  else
-    return kernel_symbol<Cfg, false>();
-}
 
 // Host-side launcher for one instantiated tuple and variant.
 // Tile rows per group of the XCD-aware order: each XCD's share of the tiles
@@ -1211,11 +1204,7 @@ hipError_t launch_tile(const KernelArgs& a, hipStream_t stream, long long slots)
   }
   const long long grid = sp.tiles_full + tail * sp.splits;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-  const void* kernel = kernel_symbol<Cfg, VEC>();
-  if constexpr (!VEC) {
-    if (a.N % 4 == 0) kernel = kernel_symbol_b16<Cfg>();
-  }
-  return hipLaunchKernel(kernel, dim3(static_cast<unsigned>(grid)),
+  return hipLaunchKernel(kernel_symbol<Cfg, VEC>(), dim3(static_cast<unsigned>(grid)),
                          dim3(Cfg::NT), args, 0, stream);
 }
 

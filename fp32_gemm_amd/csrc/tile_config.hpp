@@ -64,8 +64,8 @@ enum Opt : int {
   kOptSplitK = 8,
   // Global -> LDS with buffer loads that write LDS directly (no register
   // round-trip, no ds_write).  MFMA paths: 16-byte loads in the float4
-  // variant, 4-byte loads in the scalar variant (only for slice 0's A and,
-  // when N % 4 != 0, for B: hybrid_scalar_tile), into an As[m][k] layout
+  // variant, 4-byte loads in the scalar variant only for slice 0's A
+  // (hybrid_scalar_tile), into an As[m][k] layout
   // whose 16-byte chunks are XOR-swizzled by row; the inner product reads
   // four k of A per 128-bit LDS read.  VALU path: A keeps the transposed,
   // swizzled As[k][m] layout of register staging, filled by 4-byte loads (each
@@ -98,8 +98,8 @@ enum Opt : int {
 constexpr int stages_of(const Tile& t) { return 2 + ((t.opt & kOptStagesMask) >> kOptStagesShift); }
 
 // Tuples whose scalar variant keeps 16-byte loads for A (after the first K
-// slice) and for B when N % 4 == 0: the direct-LDS matrix-core tiles (the
-// kernels' hybrid scalar body).
+// slice) and for B: the direct-LDS matrix-core tiles (the kernels' hybrid
+// scalar body).
 constexpr bool hybrid_scalar_tile(const Tile& t) {
   return (t.opt & kOptDirectLds) != 0 && t.path != kPathValu;
 }

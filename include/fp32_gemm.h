@@ -79,7 +79,9 @@ int sgemm(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64_t 
  * whose leading dimensions are not multiples of 4, or with K or N not a
  * multiple of 4 run the scalar-load variant of the same configuration.  In
  * that variant the direct-to-LDS matrix-core configurations still load A 16
- * bytes at a time after the first K slice, and B too when N % 4 == 0. */
+ * bytes at a time after the first K slice, and B 16 bytes at a time
+ * throughout (values that a load brings from past column N reach only
+ * outputs past column N, which are never written). */
 int sgemm_ex(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64_t lda,
              const float* B, int64_t ldb, float beta, float* C, int64_t ldc, void* stream,
              int32_t cfg_id);
@@ -151,8 +153,9 @@ typedef struct sgemm_plan_t {
 /* Validates like sgemm_ex (same status codes, no device check) and fills
  * *out.  cfg_id < 0 selects the tuned configuration: the exact-shape rule;
  * else, with M, N >= 128 and K >= 32, the tile chosen from the library's
- * table of measured rates (seeded shapes of the same variant, float4 or
- * scalar, on which every table tile was timed): a measured shape's fastest
+ * table of measured rates (seeded float4-variant shapes on which every
+ * table tile was timed; a scalar-variant shape reads them among the tiles
+ * whose scalar kernel keeps 16-byte loads): a measured shape's fastest
  * tile, otherwise the tile with the highest sum over the 16 nearest measured
  * shapes in (log2 M, log2 N, log2 K), the K difference weighing 1/2, of
  * exp(-squared distance) * log(rate / that shape's best rate).  Other shapes
@@ -182,10 +185,8 @@ int sgemm_last_hip_error(void);
 int sgemm_device_check(void);
 
 /* Register/LDS/scratch use of a compiled kernel (needs a device).
- * vector_variant selects the float4 kernel (1), the scalar variant's kernel
- * for any N (0), or the scalar variant's kernel for N % 4 == 0 (2; the same
- * as 0 except for the direct-to-LDS matrix-core configurations, whose
- * scalar variant then loads B 16 bytes at a time). */
+ * vector_variant selects the float4 kernel (1) or the scalar variant's
+ * kernel (0); any other value returns SGEMM_ERR_BAD_CONFIG. */
 typedef struct sgemm_kernel_attr_t {
   int32_t num_regs;       /* architectural VGPRs reported by the runtime */
   int32_t scratch_bytes;  /* private (spill) bytes per lane */

@@ -1,6 +1,7 @@
 """The C ABI on the CPU: the library loads, exports every function the header
 declares, and validates arguments before touching any device."""
 import ctypes
+import json
 import math
 import os
 import re
@@ -200,9 +201,8 @@ def test_off_rule_shapes_follow_the_rate_table():
     # and log2 K, the K difference weighing one half) of
     # exp(-squared distance) * log(percentage / 100); a shape that is a row
     # takes that row's fastest column.  Float4 shapes read the float4 rows;
-    # scalar-variant shapes with N % 4 == 0 read them too, among the tiles
-    # whose scalar kernel keeps 16-byte loads (direct-LDS matrix-core
-    # tiles); other scalar-variant shapes read the scalar rows.
+    # scalar-variant shapes read them too, among the tiles whose scalar
+    # kernel keeps 16-byte loads (direct-LDS matrix-core tiles).
     # The choice needs no device, so this holds on any host.
     cols, scalar, vector = _rate_table()
     rules = _table_rules()
@@ -211,9 +211,8 @@ def test_off_rule_shapes_follow_the_rate_table():
         return bool(t[11] & 16) and t[9] != 0
 
     def expected(M, N, K, vec):
-        b16 = not vec and N % 4 == 0
-        rows = vector if vec or b16 else scalar
-        allowed = [c for c in range(len(cols)) if not b16 or hybrid(cols[c])]
+        rows = vector
+        allowed = [c for c in range(len(cols)) if vec or hybrid(cols[c])]
         x = (math.log2(M), math.log2(N), math.log2(K))
         d = sorted(((x[0] - math.log2(s[0])) ** 2 + (x[1] - math.log2(s[1])) ** 2 +
                     0.5 * (x[2] - math.log2(s[2])) ** 2, i) for i, (s, _) in enumerate(rows))[:16]
@@ -275,19 +274,18 @@ def test_config_table_contents():
 
 
 def test_scalar_variant_kernels_per_tuple():
-    # Direct-LDS matrix-core tuples have two scalar-variant kernels (4-byte
-    # and 16-byte B loads) in the build's resource report; every other tuple
-    # has one, which also serves N % 4 == 0.
+    # Every tuple has one scalar-variant kernel in the build's resource
+    # report; for the direct-LDS matrix-core tuples it is the hybrid kernel
+    # (16-byte loads but for slice 0's A), one per tuple.
+    with open(fg.binding._RESOURCES) as f:
+        names = list(json.load(f))
+    hyb = sum(1 for n in names if "sgemm_tile_kernel_hyb" in n)
     hybrid = 0
     for c in fg.configs():
         t = c["tuple"]
-        if t[11] & 16 and t[9] != 0:
-            hybrid += 1
-            assert c["resources_scalar_b16"] is not None
-            assert c["resources_scalar_b16"] is not c["resources_scalar"]
-        else:
-            assert c["resources_scalar_b16"] is c["resources_scalar"]
-    assert hybrid > 0
+        assert c["resources_scalar"] is not None
+        hybrid += bool(t[11] & 16 and t[9] != 0)
+    assert hybrid > 0 and hyb == hybrid
 
 
 def test_default_configs_do_not_spill():

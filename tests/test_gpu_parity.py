@@ -697,31 +697,32 @@ def test_misaligned_operands_every_direct_lds_config(fg, dev, orc):
 
 
 def test_split_plan_uses_the_launched_kernels_occupancy(fg, dev):
-    # The scalar variant of a hybrid tuple launches one of two kernels (by
-    # N % 4) whose occupancies can differ; the plan's resident slots must be
-    # the launched kernel's (its workgroups per CU times the CUs).
+    # The two variants of a tuple launch different kernels whose occupancies
+    # can differ; the plan's resident slots must be the launched kernel's
+    # (its workgroups per CU times the CUs), for N odd and N % 4 == 0 alike.
     fake = 1 << 40
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    seen = 0
+    seen = checked = 0
     for c in fg.configs():
         t = c["tuple"]
         if not (t[11] & 16 and t[9] != 0 and t[8] == 256):
             continue
-        occ0 = c["resources_scalar"]["Occupancy"]
-        occ1 = c["resources_scalar_b16"]["Occupancy"]
-        if occ0 == occ1:
-            continue
-        if (160 * 1024) // c["lds_bytes"] < max(occ0, occ1):
+        occ_s = c["resources_scalar"]["Occupancy"]
+        occ_v = c["resources_vec"]["Occupancy"]
+        if (160 * 1024) // c["lds_bytes"] < max(occ_s, occ_v):
             continue  # LDS, not registers, bounds the residency
         p0 = fg.plan(2000, 2001, 999, fake, 999, 2 * fake, 2001, 4 * fake, 2001, c["id"])
         p1 = fg.plan(2000, 2000, 999, fake, 999, 2 * fake, 2000, 4 * fake, 2000, c["id"])
-        assert p0["vector_variant"] == 0 and p1["vector_variant"] == 0
+        pv = fg.plan(2000, 2000, 1000, fake, 1000, 2 * fake, 2000, 4 * fake, 2000, c["id"])
+        assert p0["vector_variant"] == 0 and p1["vector_variant"] == 0 and pv["vector_variant"] == 1
         # 256 threads are one wave per SIMD: workgroups per CU = waves per SIMD.
-        assert p0["slots"] == cus * occ0, (t, p0["slots"], occ0)
-        assert p1["slots"] == cus * occ1, (t, p1["slots"], occ1)
-        seen += 1
-    log(f"[occupancy] {seen} tuples whose two scalar kernels differ in occupancy")
-    assert seen > 0
+        assert p0["slots"] == cus * occ_s, (t, p0["slots"], occ_s)
+        assert p1["slots"] == cus * occ_s, (t, p1["slots"], occ_s)
+        assert pv["slots"] == cus * occ_v, (t, pv["slots"], occ_v)
+        seen += occ_s != occ_v
+        checked += 1
+    log(f"[occupancy] {checked} tuples checked, {seen} whose two variants differ in occupancy")
+    assert checked > 0
 
 
 def test_transpose_identity_bit_exact(fg, dev):
