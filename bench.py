@@ -179,14 +179,13 @@ def ladder(fg, inputs, model, w, dev, args):
     print(json.dumps(out), flush=True)
 
 
-def kernel_resources(fg, info, plan, dev, N):
+def kernel_resources(fg, info, plan, dev):
     """Registers, scratch, LDS and residency of the kernel the launch ran."""
     import torch
     vec = bool(plan["vector_variant"])
-    b16 = not vec and N % 4 == 0  # the scalar variant's kernel for N % 4 == 0
-    attr = fg.binding.kernel_attributes(info["id"], 1 if vec else 2 if b16 else 0)
+    attr = fg.binding.kernel_attributes(info["id"], 1 if vec else 0)
     rep = next((c for c in fg.configs() if c["id"] == info["id"]), {})
-    res = rep.get("resources_vec" if vec else "resources_scalar_b16" if b16 else "resources_scalar") or {}
+    res = rep.get("resources_vec" if vec else "resources_scalar") or {}
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     return {"vgprs": res.get("VGPRs"), "agprs": res.get("AGPRs"),
             "sgprs": res.get("TotalSGPRs"), "scratch_bytes_per_lane": attr["scratch_bytes"],
@@ -352,7 +351,7 @@ def main():
                       "min": round(float(per.min()), 4), "max": round(float(per.max()), 4),
                       "spread": round(float((per.max() - per.min()) / np.median(per)), 4),
                       "per_launch": [round(float(x), 4) for x in per]},
-        "kernel": kernel_resources(fg, info, plan, dev, w.N),
+        "kernel": kernel_resources(fg, info, plan, dev),
     }
     if not args.no_context:
         # Warm caches: the two libraries alternate in batches of five
